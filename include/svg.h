@@ -1,0 +1,184 @@
+/*
+ * svg.h - C ABI of libsvg.so: Sparse VideoGen spatial/temporal sparse 3D
+ * attention for video diffusion transformers, native to MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *  - "Sparse Video-Gen ..." authors' rebuttal, answer to Weakness 1: a video
+ *    of N frames with F tokens each is flattened as x = i*F + j.  A spatial
+ *    head keeps pairs with |floor(x1/F) - floor(x2/F)| < a1 (a block band);
+ *    a temporal head keeps pairs with |(x1 mod F) - (x2 mod F)| < a2
+ *    (2N-1 slanted diagonals).  Answer on profiling: the head type is decided
+ *    online at every diffusion step and layer, right before attention.
+ *  - "Sparse VideoGen" abstract: online profiling predicts each head's type;
+ *    a hardware-efficient layout transformation plus custom kernels turn the
+ *    sparsity into speed.
+ *  - "Sparse-vDiT" review, "What carries the argument": per-head modes full /
+ *    skip / diagonal / multi-diagonal / vertical stripe, heads that share a
+ *    mode fused into one operation, the multi-diagonal pattern rearranged into
+ *    a diagonal one for a window kernel.
+ *
+ * Conventions for every entry point
+ *  - Tensors are [B, H, L, d] with d contiguous, L = T + N*F tokens (a text
+ *    prefix of T tokens first, then the video frame-major).  Element strides
+ *    for b, h and token are given by svg_strides; rows must be 16-byte aligned
+ *    (base pointer and every stride times the element size multiples of 16).
+ *  - All pointers except `geom`, `BM`, `BN`, `bytes` are DEVICE pointers owned
+ *    by the caller.  The library never allocates, frees or keeps a pointer;
+ *    scratch memory is the caller's workspace, sized by svg_workspace_bytes.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on it and returns; nothing synchronises.
+ *  - Return value: SVG_OK, or an error status.  On any error nothing has been
+ *    enqueued and no output was touched (except SVG_E_HIP, which reports a
+ *    failed launch); svg_last_error() then returns a message (thread-local).
+ *  - Device-side contents (modes, rows) are trusted: out-of-range values are
+ *    undefined behaviour; the Python binding can check them in debug mode.
+ */
+#ifndef SVG_H
+#define SVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVG_ABI_VERSION 1
+
+typedef enum {
+  SVG_OK = 0,
+  SVG_E_INVALID = 1,     /* bad argument (null pointer, bad size, misaligned, ...) */
+  SVG_E_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype pair, tiles) */
+  SVG_E_WORKSPACE = 3,   /* workspace missing or smaller than svg_workspace_bytes */
+  SVG_E_HIP = 4          /* the HIP runtime reported an error */
+} svg_status;
+
+typedef enum { SVG_F32 = 0, SVG_BF16 = 1 } svg_dtype;
+
+/* Per-head attention mode.  SPATIAL / TEMPORAL are the two head types of the
+ * rebuttal's Weakness 1 answer; FULL is dense attention (the profiling
+ * fallback, and Sparse-vDiT's "full"); SKIP outputs zeros; WINDOW keeps
+ * |u1-u2| < window (Sparse-vDiT "diagonal"); STRIPE keeps video keys
+ * u2 < stripe (Sparse-vDiT "vertical stripe").  u = x - T is the video index.
+ * For every mode but SKIP, text rows (x1 < T) and text keys (x2 < T) are
+ * dense. */
+typedef enum {
+  SVG_SPATIAL = 0,
+  SVG_TEMPORAL = 1,
+  SVG_FULL = 2,
+  SVG_SKIP = 3,
+  SVG_WINDOW = 4,
+  SVG_STRIPE = 5
+} svg_mode;
+
+typedef struct {
+  int32_t B, H;   /* batch, heads */
+  int32_t d;      /* head dimension: 64 or 128 */
+  int32_t N, F;   /* frames, tokens per frame (both >= 1) */
+  int32_t T;      /* text-prefix tokens (>= 0) */
+  int32_t a1, a2; /* spatial / temporal thresholds (>= 1) */
+  int32_t window; /* WINDOW width (>= 1) */
+  int32_t stripe; /* STRIPE key count (>= 1) */
+  float scale;    /* softmax scale; 0 means 1/sqrt(d) */
+} svg_geom;
+
+typedef struct {
+  int64_t b, h, x; /* element strides of batch, head and token; d is contiguous */
+} svg_strides;
+
+/* Flags of svg_sparse_attention / svg_layer_forward. */
+#define SVG_FLAG_VIRTUAL_PERMUTE 1 /* temporal heads gather rows through the
+                                      token-major index instead of reading
+                                      explicitly permuted copies */
+
+int32_t svg_abi_version(void);
+const char* svg_last_error(void);
+
+/* Query and key tile sizes (BM x BN) of the attention kernel for an input
+ * dtype and head dim; key-tile ranges must be built with exactly these.
+ * Errors: SVG_E_INVALID (null outputs), SVG_E_UNSUPPORTED (dtype/d). */
+svg_status svg_tile_config(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN);
+
+/* Workspace needed by svg_layer_forward for this geometry, input dtype,
+ * number of sampled rows (0 = no profiling) and flags.  Also covers
+ * svg_profile_heads (which needs a subset).  Writes *bytes. */
+svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_rows, int32_t flags,
+                               size_t* bytes);
+
+/* Online profiling (rebuttal: answer on when profiling happens; abstract:
+ * head types predicted online).  For every (b, h), on the n_rows sampled
+ * query rows `rows` (device int32, video rows in [T, L), shared by all heads),
+ * computes full, spatial and temporal attention in one sweep over all keys,
+ *   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
+ * and writes labels[b*H+h] = SPATIAL if rel_s <= rel_t else TEMPORAL, or FULL
+ * when min(rel_s, rel_t) >= fallback_rel_mse; stats[(b*H+h)*3 + {0,1,2}] =
+ * {rel_s, rel_t, mean O_full^2}.  Reductions are deterministic.
+ * Errors: SVG_E_INVALID / SVG_E_UNSUPPORTED / SVG_E_WORKSPACE / SVG_E_HIP. */
+svg_status svg_profile_heads(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k,
+                             const void* v, svg_strides s, const int32_t* rows, int32_t n_rows,
+                             float fallback_rel_mse, int32_t* labels, float* stats, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Key-tile lists (rebuttal Weakness 1: block-banded structure; abstract:
+ * layout transformation).  For each head (modes: device int32[B*H]) and each
+ * query tile qb of BM rows of the head's working layout (token-major for
+ * TEMPORAL heads, frame-major otherwise), writes
+ * ranges[((b*H+h)*nQT + qb)*4 + {0,1,2,3}] = {s1, e1, s2, e2}: two sorted,
+ * disjoint half-open ranges of key tiles of BN keys (empty when s == e) whose
+ * union is exactly the tiles holding an active pair.  nQT = ceil(L/BM).
+ * head_order (device int32[B*H]) lists heads by descending work (listed
+ * tiles summed over query tiles), ties by ascending head index.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED (BM/BN not multiples of 16), SVG_E_HIP. */
+svg_status svg_build_blocks(const svg_geom* geom, const int32_t* modes, int32_t BM, int32_t BN,
+                            int32_t* ranges, int32_t* head_order, void* stream);
+
+/* Layout transformation (abstract: "hardware-efficient tensor layout
+ * transformation"; Sparse-vDiT review: token rearrangement).  Forward:
+ * dst row T + j*N + i = src row T + i*F + j, text rows copied unchanged.
+ * Inverse (inverse != 0): dst row T + i*F + j = src row T + j*N + i.
+ * Applied to every (b, h) whose mode is TEMPORAL (all heads if modes NULL);
+ * other heads are left untouched.  src and dst must not overlap.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED, SVG_E_HIP. */
+svg_status svg_layout_permute(const svg_geom* geom, svg_dtype dtype, const void* src, svg_strides ss,
+                              void* dst, svg_strides ds, const int32_t* modes, int32_t inverse,
+                              void* stream);
+
+/* Block-banded sparse attention (abstract: customised kernels; Sparse-vDiT:
+ * pattern kernels with heads of one mode fused).  One launch runs every head:
+ * O = softmax(Q K^T * scale over the head's active keys) V, fp32 accumulation
+ * and softmax, bf16 (or fp32) inputs.  SKIP heads write zeros.  TEMPORAL heads
+ * run in token-major order: they read qp/kp/vp and write op (strides sp for
+ * the three inputs, sop for op), unless flags has SVG_FLAG_VIRTUAL_PERMUTE,
+ * in which case they read q/k/v and write o through the index map (qp, kp,
+ * vp, op may then be NULL).  ranges / head_order come from svg_build_blocks
+ * with the BM, BN of svg_tile_config(in, d), which are passed again here for
+ * checking.  Supported (in, out): (F32, F32), (BF16, BF16), (BF16, F32).
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED, SVG_E_HIP. */
+svg_status svg_sparse_attention(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q,
+                                const void* k, const void* v, svg_strides s, const void* qp,
+                                const void* kp, const void* vp, svg_strides sp, void* o,
+                                svg_strides so, void* op, svg_strides sop, const int32_t* modes,
+                                const int32_t* ranges, const int32_t* head_order, int32_t BM,
+                                int32_t BN, int32_t flags, void* stream);
+
+/* One attention layer of the method, as a diffusion step runs it:
+ *   modes_in == NULL: profile on `rows` (writes labels_out, stats_out), else
+ *   use modes_in (Sparse-vDiT's fixed per-head modes; no profiling, rows and
+ *   stats_out unused, labels_out receives a copy of modes_in);
+ *   build key-tile lists; permute Q, K, V of TEMPORAL heads to token-major
+ *   (skipped with SVG_FLAG_VIRTUAL_PERMUTE); sparse attention; inverse-permute
+ *   the TEMPORAL heads' output into o.
+ * labels_out: device int32[B*H]; stats_out: device float[B*H*3] (may be NULL
+ * when modes_in is given).  ws must hold svg_workspace_bytes(geom, in,
+ * modes_in ? 0 : n_rows, flags) bytes, 256-byte aligned.
+ * Errors: as the calls it makes. */
+svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q,
+                             const void* k, const void* v, svg_strides s, void* o, svg_strides so,
+                             const int32_t* rows, int32_t n_rows, float fallback_rel_mse,
+                             const int32_t* modes_in, int32_t* labels_out, float* stats_out,
+                             int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVG_H */

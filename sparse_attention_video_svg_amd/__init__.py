@@ -1,0 +1,244 @@
+"""Sparse VideoGen spatial/temporal sparse attention on MI355X (gfx950).
+
+Thin Python binding of ``libsvg.so`` (C ABI in ``include/svg.h``): argument
+marshalling only.  Every step of the path (profiling, tile lists, layout
+transformation, sparse attention) runs in the library's HIP kernels; PyTorch
+only provides device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+
+Function names equal the C entry points.  Tensors are ``[B, H, L, d]`` with
+``d`` contiguous, ``L = T + N*F``; dtype bfloat16 or float32.
+"""
+import ctypes
+import dataclasses
+import math
+import os
+
+__all__ = [
+    "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE",
+    "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config", "svg_workspace_bytes",
+    "svg_profile_heads", "svg_build_blocks", "svg_layout_permute", "svg_sparse_attention",
+    "svg_layer_forward", "library_path",
+]
+
+SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
+F32, BF16 = 0, 1
+VIRTUAL_PERMUTE = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsvg.so")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+class SvgError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"svg status {status}: {msg}")
+        self.status = status
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("F", ctypes.c_int32), ("T", ctypes.c_int32), ("a1", ctypes.c_int32), ("a2", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("stripe", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("x", ctypes.c_int64)]
+
+
+@dataclasses.dataclass
+class Geom:
+    """Geometry of one attention layer: B x H heads of width d over T text
+    tokens followed by N frames of F tokens.  a1 / a2: spatial / temporal
+    thresholds; window / stripe: Sparse-vDiT diagonal width and stripe keys;
+    scale 0 means 1/sqrt(d)."""
+    B: int
+    H: int
+    d: int
+    N: int
+    F: int
+    T: int = 0
+    a1: int = 1
+    a2: int = 1
+    window: int = 1
+    stripe: int = 1
+    scale: float = 0.0
+
+    @property
+    def L(self):
+        return self.T + self.N * self.F
+
+    def c(self):
+        return _Geom(self.B, self.H, self.d, self.N, self.F, self.T, self.a1, self.a2, self.window,
+                     self.stripe, float(self.scale))
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                               "python -m sparse_attention_video_svg_amd._build")
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER
+        g = P(_Geom)
+        S = _Strides
+        vp = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        sig = {
+            "svg_abi_version": ([], i32),
+            "svg_last_error": ([], ctypes.c_char_p),
+            "svg_tile_config": ([i32, i32, P(i32), P(i32)], i32),
+            "svg_workspace_bytes": ([g, i32, i32, i32, P(ctypes.c_size_t)], i32),
+            "svg_profile_heads": ([g, i32, vp, vp, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp],
+                                  i32),
+            "svg_build_blocks": ([g, vp, i32, i32, vp, vp, vp], i32),
+            "svg_layout_permute": ([g, i32, vp, S, vp, S, vp, i32, vp], i32),
+            "svg_sparse_attention": ([g, i32, i32, vp, vp, vp, S, vp, vp, vp, S, vp, S, vp, S, vp, vp, vp, i32, i32,
+                                      i32, vp], i32),
+            "svg_layer_forward": ([g, i32, i32, vp, vp, vp, S, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, i32, vp,
+                                   ctypes.c_size_t, vp], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(status):
+    if status != 0:
+        raise SvgError(status, svg_last_error())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t):
+    """Element strides (b, h, x) of a [B, H, L, d] tensor with d contiguous."""
+    if t is None:
+        return _Strides(0, 0, 0)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("tensors must be [B, H, L, d] with d contiguous")
+    return _Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_shape(geom, t, name):
+    if tuple(t.shape) != (geom.B, geom.H, geom.L, geom.d):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(geom.B, geom.H, geom.L, geom.d)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def svg_abi_version():
+    return _lib().svg_abi_version()
+
+
+def svg_last_error():
+    msg = _lib().svg_last_error()
+    return msg.decode() if msg else ""
+
+
+def svg_tile_config(dtype, d):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib().svg_tile_config(dtype, d, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def svg_workspace_bytes(geom, dtype, n_rows=0, flags=0):
+    n = ctypes.c_size_t()
+    g = geom.c()
+    _check(_lib().svg_workspace_bytes(ctypes.byref(g), dtype, n_rows, flags, ctypes.byref(n)))
+    return n.value
+
+
+def svg_profile_heads(geom, q, k, v, rows, labels, stats, ws, fallback_rel_mse=0.05, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    g = geom.c()
+    _check(_lib().svg_profile_heads(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _strides(q),
+                                    _ptr(rows), rows.numel(), float(fallback_rel_mse), _ptr(labels), _ptr(stats),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def svg_build_blocks(geom, modes, BM, BN, ranges, head_order, stream=None):
+    g = geom.c()
+    _check(_lib().svg_build_blocks(ctypes.byref(g), _ptr(modes), BM, BN, _ptr(ranges), _ptr(head_order),
+                                   _stream(stream)))
+
+
+def svg_layout_permute(geom, src, dst, modes=None, inverse=False, stream=None):
+    _check_shape(geom, src, "src")
+    _check_shape(geom, dst, "dst")
+    if src.dtype != dst.dtype:
+        raise TypeError("src and dst dtypes differ")
+    g = geom.c()
+    _check(_lib().svg_layout_permute(ctypes.byref(g), _dtype_code(src), _ptr(src), _strides(src), _ptr(dst),
+                                     _strides(dst), _ptr(modes), 1 if inverse else 0, _stream(stream)))
+
+
+def svg_sparse_attention(geom, q, k, v, o, modes, ranges, head_order, qp=None, kp=None, vp=None, op=None,
+                         flags=0, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    if qp is not None and (kp.stride() != qp.stride() or vp.stride() != qp.stride()):
+        raise ValueError("qp, kp and vp must share strides")
+    din = _dtype_code(q)
+    BM, BN = svg_tile_config(din, geom.d)
+    g = geom.c()
+    _check(_lib().svg_sparse_attention(
+        ctypes.byref(g), din, _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(qp), _ptr(kp), _ptr(vp),
+        _strides(qp), _ptr(o), _strides(o), _ptr(op), _strides(op), _ptr(modes), _ptr(ranges), _ptr(head_order),
+        BM, BN, flags, _stream(stream)))
+
+
+def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_out=None, modes_in=None,
+                      fallback_rel_mse=0.05, flags=0, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    g = geom.c()
+    n_rows = 0 if rows is None else rows.numel()
+    _check(_lib().svg_layer_forward(
+        ctypes.byref(g), _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(o),
+        _strides(o), _ptr(rows), n_rows, float(fallback_rel_mse), _ptr(modes_in), _ptr(labels_out),
+        _ptr(stats_out), flags, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def alloc_workspace(geom, dtype, n_rows=0, flags=0, device="cuda"):
+    """Workspace tensor (uint8, 256-byte aligned by the caching allocator)."""
+    import torch
+    n = svg_workspace_bytes(geom, dtype, n_rows, flags)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

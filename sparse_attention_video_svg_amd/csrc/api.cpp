@@ -1,0 +1,370 @@
+// C ABI of libsvg.so (declared in include/svg.h): argument validation,
+// workspace layout and the order of launches of one attention layer.
+//
+// Every entry point validates all of its host-visible arguments before it
+// makes any HIP call, so an invalid call enqueues nothing; this also makes the
+// validation testable on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "svg_internal.h"
+
+using namespace svg;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+svg_status fail(svg_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+svg_status hip_fail(hipError_t e, const char* where) {
+  return fail(SVG_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+constexpr int32_t kMaxHeads = 4096;
+
+int elt_bytes(svg_dtype t) { return t == SVG_BF16 ? 2 : 4; }
+bool dtype_ok(int t) { return t == SVG_F32 || t == SVG_BF16; }
+
+svg_status check_geom(const svg_geom* geom, KGeom* out) {
+  if (!geom) return fail(SVG_E_INVALID, "geom is NULL");
+  const svg_geom& g = *geom;
+  if (g.B < 1 || g.H < 1) return fail(SVG_E_INVALID, "B and H must be >= 1 (got %d, %d)", g.B, g.H);
+  if ((int64_t)g.B * g.H > kMaxHeads) return fail(SVG_E_UNSUPPORTED, "B*H > %d", kMaxHeads);
+  if (g.d != 64 && g.d != 128) return fail(SVG_E_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", g.d);
+  if (g.N < 1 || g.F < 1) return fail(SVG_E_INVALID, "N and F must be >= 1 (got %d, %d)", g.N, g.F);
+  if (g.T < 0) return fail(SVG_E_INVALID, "T must be >= 0 (got %d)", g.T);
+  if (g.a1 < 1 || g.a2 < 1) return fail(SVG_E_INVALID, "a1 and a2 must be >= 1 (got %d, %d)", g.a1, g.a2);
+  if (g.window < 1 || g.stripe < 1)
+    return fail(SVG_E_INVALID, "window and stripe must be >= 1 (got %d, %d)", g.window, g.stripe);
+  const int64_t L = (int64_t)g.T + (int64_t)g.N * g.F;
+  if (L > kMaxTokens) return fail(SVG_E_UNSUPPORTED, "T + N*F = %lld tokens exceeds 2^30", (long long)L);
+  if (!(isfinite(g.scale) && g.scale >= 0.f)) return fail(SVG_E_INVALID, "scale must be finite and >= 0");
+  if (out) {
+    KGeom& k = *out;
+    k.B = g.B;
+    k.H = g.H;
+    k.d = g.d;
+    k.N = g.N;
+    k.F = g.F;
+    k.T = g.T;
+    k.a1 = g.a1;
+    k.a2 = g.a2;
+    k.window = g.window;
+    k.stripe = g.stripe;
+    k.L = (int32_t)L;
+    k.scale = g.scale > 0.f ? g.scale : (float)(1.0 / sqrt((double)g.d));
+    k.scale_log2 = (float)((double)k.scale * 1.4426950408889634);
+    fastdiv_init((uint32_t)g.N, &k.divN_mul, &k.divN_shift);
+    fastdiv_init((uint32_t)g.F, &k.divF_mul, &k.divF_shift);
+  }
+  return SVG_OK;
+}
+
+svg_status check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(SVG_E_INVALID, "%s is NULL", name);
+  if (((uintptr_t)p) % align) return fail(SVG_E_INVALID, "%s is not %zu-byte aligned", name, align);
+  return SVG_OK;
+}
+
+svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const char* name) {
+  if (s.x < g.d) return fail(SVG_E_INVALID, "%s: token stride %lld < d", name, (long long)s.x);
+  if (s.h < 0 || s.b < 0) return fail(SVG_E_INVALID, "%s: negative stride", name);
+  if ((s.x * elt) % 16 || (s.h * elt) % 16 || (s.b * elt) % 16)
+    return fail(SVG_E_INVALID, "%s: strides must be multiples of 16 bytes", name);
+  return SVG_OK;
+}
+
+#define TRY(expr)                      \
+  do {                                 \
+    svg_status _st = (expr);           \
+    if (_st != SVG_OK) return _st;     \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
+  if (dtype != SVG_BF16) return 1;
+  const int64_t chunks = (n_rows + kProfRows_bf16 - 1) / kProfRows_bf16;
+  const int64_t wgs = chunks * g.B * g.H;
+  int64_t ks = (1024 + wgs - 1) / wgs;
+  const int64_t nkt = (g.L + kBN_bf16 - 1) / kBN_bf16;
+  if (ks > 16) ks = 16;
+  if (ks > nkt) ks = nkt;
+  if (ks < 1) ks = 1;
+  return (int32_t)ks;
+}
+
+// Layout: [profiling partials][labels][ranges][head order][permuted Q,K,V,O].
+WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flags) {
+  WsLayout w{};
+  const int64_t BH = (int64_t)g.B * g.H;
+  const int32_t BM = dtype == SVG_BF16 ? kBM_bf16 : kBM_f32;
+  const int64_t nQT = (g.L + BM - 1) / BM;
+  size_t off = 0;
+  w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows) : 0;
+  w.part_acc = off;
+  off = align256(off + sizeof(float) * (size_t)BH * n_rows * w.ksplit * 3 * g.d);
+  w.part_ml = off;
+  off = align256(off + sizeof(float) * (size_t)BH * n_rows * w.ksplit * 3 * 2);
+  w.labels = off;
+  off = align256(off + sizeof(int32_t) * (size_t)BH);
+  w.ranges = off;
+  off = align256(off + sizeof(int32_t) * 4 * (size_t)BH * nQT);
+  w.order = off;
+  off = align256(off + sizeof(int32_t) * (size_t)BH);
+  w.perm = off;
+  w.perm_tensor_bytes = 0;
+  if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
+    // token-major Q, K, V in the input dtype, then O sized for fp32 output
+    w.perm_tensor_bytes = align256((size_t)BH * g.L * g.d * elt_bytes(dtype));
+    off += 3 * w.perm_tensor_bytes + align256((size_t)BH * g.L * g.d * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+size_t profile_ws_bytes(const WsLayout& w) { return w.labels; }
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+svg_status tile_config_impl(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN) {
+  if (!dtype_ok(dtype)) return fail(SVG_E_INVALID, "unknown dtype %d", (int)dtype);
+  if (d != 64 && d != 128) return fail(SVG_E_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (dtype == SVG_BF16) {
+    *BM = kBM_bf16;
+    *BN = kBN_bf16;
+  } else {
+    *BM = kBM_f32;
+    *BN = kBN_f32;
+  }
+  return SVG_OK;
+}
+
+svg_status validate_attention(const KGeom& g, svg_dtype in, svg_dtype out, const void* q, const void* k,
+                              const void* v, svg_strides s, const void* qp, const void* kp, const void* vp,
+                              svg_strides sp, const void* o, svg_strides so, const void* op, svg_strides sop,
+                              const int32_t* modes, const int32_t* ranges, const int32_t* order, int32_t BM,
+                              int32_t BN, int32_t flags) {
+  if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
+  if (in == SVG_F32 && out != SVG_F32) return fail(SVG_E_UNSUPPORTED, "f32 input requires f32 output");
+  if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  int32_t bm, bn;
+  TRY(tile_config_impl(in, g.d, &bm, &bn));
+  if (BM != bm || BN != bn)
+    return fail(SVG_E_UNSUPPORTED, "ranges built with %dx%d tiles; this kernel needs %dx%d", BM, BN, bm, bn);
+  const int ei = elt_bytes(in), eo = elt_bytes(out);
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(k, "k", 16));
+  TRY(check_ptr(v, "v", 16));
+  TRY(check_ptr(o, "o", 16));
+  TRY(check_strides(s, g, ei, "q/k/v"));
+  TRY(check_strides(so, g, eo, "o"));
+  if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
+    TRY(check_ptr(qp, "qp", 16));
+    TRY(check_ptr(kp, "kp", 16));
+    TRY(check_ptr(vp, "vp", 16));
+    TRY(check_ptr(op, "op", 16));
+    TRY(check_strides(sp, g, ei, "qp/kp/vp"));
+    TRY(check_strides(sop, g, eo, "op"));
+  }
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(ranges, "ranges", 16));
+  TRY(check_ptr(order, "head_order", 4));
+  return SVG_OK;
+}
+
+hipError_t run_attention(const KGeom& g, svg_dtype in, svg_dtype out, const AttnPtrs& a, hipStream_t st) {
+  if (in == SVG_BF16) return launch_attention_bf16(g, a, out == SVG_BF16, st);
+  return launch_attention_f32(g, a, kBM_f32, kBN_f32, st);
+}
+
+svg_status validate_profile(const KGeom& g, svg_dtype dtype, const void* q, const void* k, const void* v,
+                            svg_strides s, const int32_t* rows, int32_t n_rows, float fallback,
+                            const int32_t* labels, const float* stats) {
+  if (!dtype_ok(dtype)) return fail(SVG_E_INVALID, "unknown dtype %d", (int)dtype);
+  const int e = elt_bytes(dtype);
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(k, "k", 16));
+  TRY(check_ptr(v, "v", 16));
+  TRY(check_strides(s, g, e, "q/k/v"));
+  TRY(check_ptr(rows, "rows", 4));
+  if (n_rows < 1 || (int64_t)n_rows > (int64_t)g.N * g.F)
+    return fail(SVG_E_INVALID, "n_rows=%d must be in [1, N*F]", n_rows);
+  if (!(fallback > 0.f) || !isfinite(fallback)) return fail(SVG_E_INVALID, "fallback_rel_mse must be > 0");
+  TRY(check_ptr(labels, "labels", 4));
+  TRY(check_ptr(stats, "stats", 4));
+  return SVG_OK;
+}
+
+hipError_t run_profile(const KGeom& g, svg_dtype dtype, const void* q, const void* k, const void* v,
+                       svg_strides s, const int32_t* rows, int32_t n_rows, float fallback, int32_t* labels,
+                       float* stats, void* ws, const WsLayout& w, hipStream_t st) {
+  float* pa = ws_at<float>(ws, w.part_acc);
+  float* pm = ws_at<float>(ws, w.part_ml);
+  hipError_t e = dtype == SVG_BF16 ? launch_profile_bf16(g, q, k, v, s, rows, n_rows, w.ksplit, pa, pm, st)
+                                   : launch_profile_f32(g, q, k, v, s, rows, n_rows, pa, pm, st);
+  if (e != hipSuccess) return e;
+  return launch_profile_merge(g, n_rows, w.ksplit, pa, pm, fallback, labels, stats, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t svg_abi_version(void) { return SVG_ABI_VERSION; }
+
+const char* svg_last_error(void) { return g_err; }
+
+svg_status svg_tile_config(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN) {
+  if (!BM || !BN) return fail(SVG_E_INVALID, "BM/BN output pointer is NULL");
+  return tile_config_impl(dtype, d, BM, BN);
+}
+
+svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_rows, int32_t flags,
+                               size_t* bytes) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(dtype)) return fail(SVG_E_INVALID, "unknown dtype %d", (int)dtype);
+  if (!bytes) return fail(SVG_E_INVALID, "bytes is NULL");
+  if (n_rows < 0 || (int64_t)n_rows > (int64_t)g.N * g.F)
+    return fail(SVG_E_INVALID, "n_rows=%d must be in [0, N*F]", n_rows);
+  if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  *bytes = ws_layout(g, dtype, n_rows, flags).total;
+  return SVG_OK;
+}
+
+svg_status svg_profile_heads(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k, const void* v,
+                             svg_strides s, const int32_t* rows, int32_t n_rows, float fallback_rel_mse,
+                             int32_t* labels, float* stats, void* ws, size_t ws_bytes, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  TRY(validate_profile(g, dtype, q, k, v, s, rows, n_rows, fallback_rel_mse, labels, stats));
+  const WsLayout w = ws_layout(g, dtype, n_rows, SVG_FLAG_VIRTUAL_PERMUTE);
+  TRY(check_ptr(ws, "ws", 256));
+  if (ws_bytes < profile_ws_bytes(w))
+    return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, profile_ws_bytes(w));
+  hipError_t e = run_profile(g, dtype, q, k, v, s, rows, n_rows, fallback_rel_mse, labels, stats, ws, w,
+                             (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_profile_heads");
+}
+
+svg_status svg_build_blocks(const svg_geom* geom, const int32_t* modes, int32_t BM, int32_t BN, int32_t* ranges,
+                            int32_t* head_order, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (BM < 16 || BN < 16 || BM > 1024 || BN > 1024 || BM % 16 || BN % 16)
+    return fail(SVG_E_UNSUPPORTED, "tile sizes %dx%d must be multiples of 16 in [16, 1024]", BM, BN);
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(ranges, "ranges", 16));
+  TRY(check_ptr(head_order, "head_order", 4));
+  hipError_t e = launch_build_blocks(g, modes, BM, BN, ranges, head_order, (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_build_blocks");
+}
+
+svg_status svg_layout_permute(const svg_geom* geom, svg_dtype dtype, const void* src, svg_strides ss, void* dst,
+                              svg_strides ds, const int32_t* modes, int32_t inverse, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(dtype)) return fail(SVG_E_INVALID, "unknown dtype %d", (int)dtype);
+  const int e = elt_bytes(dtype);
+  TRY(check_ptr(src, "src", 16));
+  TRY(check_ptr(dst, "dst", 16));
+  TRY(check_strides(ss, g, e, "src"));
+  TRY(check_strides(ds, g, e, "dst"));
+  if (src == dst) return fail(SVG_E_INVALID, "src and dst must not overlap");
+  if (modes) TRY(check_ptr(modes, "modes", 4));
+  hipError_t he = launch_permute(g, e, src, ss, dst, ds, modes, inverse ? 1 : 0, (hipStream_t)stream);
+  return he == hipSuccess ? SVG_OK : hip_fail(he, "svg_layout_permute");
+}
+
+svg_status svg_sparse_attention(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q, const void* k,
+                                const void* v, svg_strides s, const void* qp, const void* kp, const void* vp,
+                                svg_strides sp, void* o, svg_strides so, void* op, svg_strides sop,
+                                const int32_t* modes, const int32_t* ranges, const int32_t* head_order,
+                                int32_t BM, int32_t BN, int32_t flags, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  TRY(validate_attention(g, in, out, q, k, v, s, qp, kp, vp, sp, o, so, op, sop, modes, ranges, head_order, BM,
+                         BN, flags));
+  AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sop, modes, ranges, head_order, flags};
+  hipError_t e = run_attention(g, in, out, a, (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention");
+}
+
+svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q, const void* k,
+                             const void* v, svg_strides s, void* o, svg_strides so, const int32_t* rows,
+                             int32_t n_rows, float fallback_rel_mse, const int32_t* modes_in, int32_t* labels_out,
+                             float* stats_out, int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
+  if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  const bool profile = modes_in == nullptr;
+  if (profile) {
+    TRY(validate_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out));
+  } else {
+    TRY(check_ptr(modes_in, "modes_in", 4));
+    if (labels_out) TRY(check_ptr(labels_out, "labels_out", 4));
+  }
+  const WsLayout w = ws_layout(g, in, profile ? n_rows : 0, flags);
+  TRY(check_ptr(ws, "ws", 256));
+  if (ws_bytes < w.total) return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  int32_t BM, BN;
+  TRY(tile_config_impl(in, g.d, &BM, &BN));
+  const bool virt = flags & SVG_FLAG_VIRTUAL_PERMUTE;
+  const int ei = elt_bytes(in), eo = elt_bytes(out);
+  const svg_strides sp{(int64_t)g.H * g.L * g.d, (int64_t)g.L * g.d, g.d};
+  char* perm = ws_at<char>(ws, w.perm);
+  void* qp = virt ? nullptr : perm;
+  void* kp = virt ? nullptr : perm + w.perm_tensor_bytes;
+  void* vp = virt ? nullptr : perm + 2 * w.perm_tensor_bytes;
+  void* op = virt ? nullptr : perm + 3 * w.perm_tensor_bytes;
+  int32_t* ranges = ws_at<int32_t>(ws, w.ranges);
+  int32_t* order = ws_at<int32_t>(ws, w.order);
+  TRY(validate_attention(g, in, out, q, k, v, s, qp, kp, vp, sp, o, so, op, sp, profile ? labels_out : modes_in,
+                         ranges, order, BM, BN, flags));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  const int32_t* modes = modes_in;
+  if (profile) {
+    e = run_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out, ws, w, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (profiling)");
+    modes = labels_out;
+  } else if (labels_out && labels_out != modes_in) {
+    e = hipMemcpyAsync(labels_out, modes_in, sizeof(int32_t) * g.B * g.H, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (labels copy)");
+  }
+  e = launch_build_blocks(g, modes, BM, BN, ranges, order, st);
+  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (blocks)");
+  if (!virt) {
+    const void* src[3] = {q, k, v};
+    void* dst[3] = {qp, kp, vp};
+    for (int t = 0; t < 3; ++t) {
+      e = launch_permute(g, ei, src[t], s, dst[t], sp, modes, 0, st);
+      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (permute)");
+    }
+  }
+  AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sp, modes, ranges, order, flags};
+  e = run_attention(g, in, out, a, st);
+  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (attention)");
+  if (!virt) {
+    e = launch_permute(g, eo, op, sp, o, so, modes, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (inverse permute)");
+  }
+  return SVG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal declarations shared by the host-side API and the kernel files of
+// libsvg.so.  Not part of the public ABI (that is include/svg.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "svg.h"
+
+namespace svg {
+
+// Geometry as the kernels see it (passed by value).
+struct KGeom {
+  int32_t B, H, d, N, F, T, a1, a2, window, stripe;
+  int32_t L;          // T + N*F
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  // invariant-divisor constants for x/N and x/F (see FastDiv)
+  uint32_t divN_mul, divN_shift, divF_mul, divF_shift;
+};
+
+// Division of a non-negative int32 by an invariant positive divisor with one
+// multiply-high, after Granlund and Montgomery, "Division by invariant
+// integers using multiplication" (PLDI 1994): with s = ceil(log2 dv) and
+// m = floor(2^32 (2^s - dv) / dv) + 1, n / dv = (mulhi(n, m) + n) >> s for
+// 0 <= n < 2^31.
+inline void fastdiv_init(uint32_t dv, uint32_t* mul, uint32_t* shift) {
+  uint32_t s = 0;
+  while ((1ull << s) < dv) ++s;
+  uint64_t m = ((1ull << 32) * ((1ull << s) - dv)) / dv + 1;
+  *mul = (uint32_t)m;
+  *shift = s;
+}
+
+__device__ __forceinline__ int32_t fastdiv(int32_t n, uint32_t mul, uint32_t shift) {
+  uint32_t hi = __umulhi((uint32_t)n, mul);
+  return (int32_t)((hi + (uint32_t)n) >> shift);
+}
+
+// Workspace carve-up for svg_layer_forward / svg_profile_heads.
+struct WsLayout {
+  size_t labels, ranges, order, part_acc, part_ml, perm, total;
+  size_t perm_tensor_bytes;  // one permuted tensor (all heads)
+  int32_t ksplit;            // key splits of the profiling sweep
+};
+
+// Launchers (each returns hipGetLastError() after its launches).
+hipError_t launch_build_blocks(const KGeom& g, const int32_t* modes, int32_t BM, int32_t BN,
+                               int32_t* ranges, int32_t* head_order, hipStream_t st);
+hipError_t launch_permute(const KGeom& g, int elt_bytes, const void* src, svg_strides ss, void* dst,
+                          svg_strides ds, const int32_t* modes, int inverse, hipStream_t st);
+
+struct AttnPtrs {
+  const void *q, *k, *v, *qp, *kp, *vp;
+  void *o, *op;
+  svg_strides s, sp, so, sop;
+  const int32_t *modes, *ranges, *order;
+  int32_t flags;
+};
+hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, int32_t BN, hipStream_t st);
+hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st);
+
+// Profiling: partial sweeps write (m, l, acc) per (head, row, split, state);
+// the merge kernel reduces them, deterministically, into labels and stats.
+hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
+                              const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml,
+                              hipStream_t st);
+hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
+                               const int32_t* rows, int32_t n_rows, int32_t ksplit, float* part_acc,
+                               float* part_ml, hipStream_t st);
+hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
+                                const float* part_ml, float fallback, int32_t* labels, float* stats,
+                                hipStream_t st);
+
+// Tile sizes of the bf16 MFMA attention kernel and of the fp32 kernel.
+constexpr int32_t kBM_bf16 = 128, kBN_bf16 = 64;
+constexpr int32_t kBM_f32 = 64, kBN_f32 = 64;
+// Query rows per workgroup of the bf16 profiling sweep.
+constexpr int32_t kProfRows_bf16 = 128;
+
+}  // namespace svg

@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/svg.h declares, and rejects invalid arguments with the
+documented status before it makes any HIP call (so nothing is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_video_svg_amd as svg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svg.h")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["svg_abi_version", "svg_last_error", "svg_tile_config", "svg_workspace_bytes", "svg_profile_heads",
+              "svg_build_blocks", "svg_layout_permute", "svg_sparse_attention", "svg_layer_forward"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(svg.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", svg.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (svg_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert svg.svg_abi_version() == 1
+
+
+def test_python_binding_has_the_same_names():
+    for n in declared_functions():
+        assert callable(getattr(svg, n)), n
+
+
+def test_tile_config():
+    assert svg.svg_tile_config(svg.BF16, 128) == (128, 64)
+    assert svg.svg_tile_config(svg.BF16, 64) == (128, 64)
+    assert svg.svg_tile_config(svg.F32, 64) == (64, 64)
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_tile_config(svg.BF16, 96)
+    assert e.value.status == E_UNSUPPORTED
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_tile_config(7, 64)
+    assert e.value.status == E_INVALID
+
+
+def geom(**kw):
+    g = dict(B=1, H=2, d=128, N=4, F=64, T=0, a1=2, a2=8, window=64, stripe=16, scale=0.0)
+    g.update(kw)
+    return svg.Geom(**g)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), E_INVALID), (dict(H=0), E_INVALID), (dict(d=96), E_UNSUPPORTED), (dict(N=0), E_INVALID),
+    (dict(F=0), E_INVALID), (dict(T=-1), E_INVALID), (dict(a1=0), E_INVALID), (dict(a2=0), E_INVALID),
+    (dict(window=0), E_INVALID), (dict(stripe=0), E_INVALID), (dict(scale=-1.0), E_INVALID),
+    (dict(scale=float("inf")), E_INVALID), (dict(H=5000), E_UNSUPPORTED), (dict(N=1 << 16, F=1 << 15), E_UNSUPPORTED),
+])
+def test_geometry_validation(kw, status):
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_workspace_bytes(geom(**kw), svg.BF16, 0, 0)
+    assert e.value.status == status
+    assert svg.svg_last_error()
+
+
+def test_workspace_bytes_grows_with_rows_and_explicit_permutation():
+    g = geom()
+    a = svg.svg_workspace_bytes(g, svg.BF16, 0, svg.VIRTUAL_PERMUTE)
+    b = svg.svg_workspace_bytes(g, svg.BF16, 16, svg.VIRTUAL_PERMUTE)
+    c = svg.svg_workspace_bytes(g, svg.BF16, 16, 0)
+    assert 0 < a < b < c
+    L = g.L
+    assert c - b >= 3 * g.H * L * g.d * 2 + g.H * L * g.d * 4
+    with pytest.raises(svg.SvgError):
+        svg.svg_workspace_bytes(g, svg.BF16, g.N * g.F + 1, 0)
+    with pytest.raises(svg.SvgError):
+        svg.svg_workspace_bytes(g, svg.BF16, 0, 8)
+
+
+# Raw calls with fake (aligned, never dereferenced) device addresses: each
+# must fail in validation, before any HIP call.
+A = 0x10000  # 16-byte aligned fake address
+
+
+def raw():
+    return svg._lib()
+
+
+def strides(b=4 * 64 * 128, h=64 * 128 * 0 + 256 * 128, x=128):
+    return svg._Strides(b, h, x)
+
+
+def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, modes=A, ranges=A, order=A,
+                   BM=128, BN=64, flags=0, qp=A, sp=None):
+    gc = g.c()
+    s = s or strides()
+    so = so or strides()
+    sp = sp or strides()
+    return raw().svg_sparse_attention(ctypes.byref(gc), din, dout, q, A, A, s, qp, A, A, sp, o, so, A, sp, modes,
+                                      ranges, order, BM, BN, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_INVALID), (dict(q=A + 8), E_INVALID), (dict(o=None), E_INVALID),
+    (dict(modes=None), E_INVALID), (dict(ranges=None), E_INVALID), (dict(order=None), E_INVALID),
+    (dict(BM=64), E_UNSUPPORTED), (dict(BN=128), E_UNSUPPORTED), (dict(din=svg.F32, dout=svg.BF16), E_UNSUPPORTED),
+    (dict(din=5), E_INVALID), (dict(flags=4), E_INVALID), (dict(qp=None), E_INVALID),
+    (dict(s=svg._Strides(0, 0, 64)), E_INVALID), (dict(s=svg._Strides(0, 0, 132)), E_INVALID),
+    (dict(so=svg._Strides(-8, 0, 128)), E_INVALID),
+])
+def test_attention_validation(kw, status):
+    assert call_attention(geom(), **kw) == status
+    assert svg.svg_last_error()
+
+
+def test_profile_validation():
+    g = geom().c()
+    L = raw()
+    s = strides()
+    base = dict(q=A, rows=A, n=8, fb=0.05, labels=A, stats=A, ws=A, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.svg_profile_heads(ctypes.byref(g), svg.BF16, a["q"], A, A, s, a["rows"], a["n"], a["fb"],
+                                   a["labels"], a["stats"], a["ws"], a["wsb"], None)
+
+    assert call(rows=None) == E_INVALID
+    assert call(n=0) == E_INVALID
+    assert call(n=4 * 64 + 1) == E_INVALID
+    assert call(fb=0.0) == E_INVALID
+    assert call(fb=float("nan")) == E_INVALID
+    assert call(labels=None) == E_INVALID
+    assert call(ws=None) == E_INVALID
+    assert call(ws=A + 16) == E_INVALID
+    assert call(wsb=16) == E_WORKSPACE
+
+
+def test_blocks_permute_layer_validation():
+    g = geom().c()
+    L = raw()
+    assert L.svg_build_blocks(ctypes.byref(g), A, 100, 64, A, A, None) == E_UNSUPPORTED
+    assert L.svg_build_blocks(ctypes.byref(g), None, 128, 64, A, A, None) == E_INVALID
+    assert L.svg_build_blocks(None, A, 128, 64, A, A, None) == E_INVALID
+    s = strides()
+    assert L.svg_layout_permute(ctypes.byref(g), svg.BF16, A, s, A, s, None, 0, None) == E_INVALID  # overlap
+    assert L.svg_layout_permute(ctypes.byref(g), svg.BF16, None, s, A, s, None, 0, None) == E_INVALID
+    assert L.svg_layout_permute(ctypes.byref(g), 3, A, s, A + 4096, s, None, 0, None) == E_INVALID
+    # layer: too small a workspace, bad flags, missing labels when profiling
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A, 0, A,
+                               1024, None) == E_WORKSPACE
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A, 2, A,
+                               1 << 40, None) == E_INVALID
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, None, A, 0,
+                               A, 1 << 40, None) == E_INVALID

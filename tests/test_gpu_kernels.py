@@ -1,0 +1,181 @@
+"""GPU parity of every kernel family against the CPU oracle on small shapes
+that still span several tiles and end in ragged tails (marked gpu).
+
+Bars: layout transformation, tile lists and head labels bit-exact; attention
+max-abs <= 2e-2 and RMS <= 2e-3 for bf16 inputs, max-abs <= 1e-5 for fp32."""
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_video_svg_amd as svg
+import svg_synth as S
+from helpers import (block_bitmap_from_ranges, check_close, ogeom, scale_of, to_device)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MODES6 = [svg.SPATIAL, svg.TEMPORAL, svg.FULL, svg.SKIP, svg.WINDOW, svg.STRIPE]
+
+
+def planted_kind(mode):
+    return {svg.SPATIAL: S.SPATIAL, svg.TEMPORAL: S.TEMPORAL, svg.FULL: S.FULL, svg.SKIP: S.FULL,
+            svg.WINDOW: S.WINDOW, svg.STRIPE: S.STRIPE}[mode]
+
+
+@pytest.mark.parametrize("dt,N,F,T,d,pad", [
+    ("bf16", 5, 37, 3, 64, 0), ("bf16", 7, 9, 0, 128, 8), ("bf16", 33, 20, 70, 128, 0),
+    ("f32", 3, 40, 5, 64, 4), ("f32", 4, 64, 0, 128, 0)])
+def test_layout_permute_bit_exact(dt, N, F, T, d, pad):
+    B, H = 2, 3
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T)
+    L = g.L
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    idt = torch.int16 if dt == "bf16" else torch.int32
+    gen = torch.Generator().manual_seed(N * 1000 + F)
+    base = torch.randint(-30000, 30000, (B, H, L, d + pad), generator=gen, dtype=torch.int32).to(idt)
+    src = base.cuda().view(tdt)[..., :d]
+    dst = torch.full((B, H, L, d), 7, dtype=idt).cuda().view(tdt)
+    modes = torch.tensor([svg.TEMPORAL, svg.SPATIAL, svg.TEMPORAL, svg.FULL, svg.TEMPORAL, svg.SKIP],
+                         dtype=torch.int32).cuda()
+    svg.svg_layout_permute(g, src, dst, modes=modes)
+    back = torch.full_like(dst, 0)
+    svg.svg_layout_permute(g, dst, back, modes=modes, inverse=True)
+    allp = torch.empty_like(dst)
+    svg.svg_layout_permute(g, src, allp)
+    torch.cuda.synchronize()
+    og = oracle.geom(N, F, T)
+    src_np = base[..., :d].numpy()
+    dst_np = dst.view(idt).cpu().numpy()
+    back_np = back.view(idt).cpu().numpy()
+    all_np = allp.view(idt).cpu().numpy()
+    m = modes.cpu().numpy().reshape(B, H)
+    for b in range(B):
+        for h in range(H):
+            want = oracle.permute_rows(og, np.ascontiguousarray(src_np[b, h]))
+            assert np.array_equal(all_np[b, h], want)
+            if m[b, h] == svg.TEMPORAL:
+                assert np.array_equal(dst_np[b, h], want)
+                assert np.array_equal(back_np[b, h], src_np[b, h])
+            else:  # untouched
+                assert np.all(dst_np[b, h] == 7)
+                assert np.all(back_np[b, h] == 0)
+
+
+@pytest.mark.parametrize("N,F,T,a1,a2,W,St,BM,BN", [
+    (5, 37, 3, 2, 5, 40, 100, 128, 64), (33, 60, 0, 2, 7, 60, 512, 128, 64), (4, 64, 0, 1, 8, 64, 16, 64, 64),
+    (13, 50, 256, 3, 11, 25, 70, 128, 64), (3, 31, 17, 1, 40, 5, 1, 32, 16)])
+def test_build_blocks_bit_exact(N, F, T, a1, a2, W, St, BM, BN):
+    H = 6
+    g = svg.Geom(B=2, H=H, d=128, N=N, F=F, T=T, a1=a1, a2=a2, window=W, stripe=St)
+    L = g.L
+    nq, nk = -(-L // BM), -(-L // BN)
+    modes_np = np.array(MODES6 + MODES6[::-1], dtype=np.int32)
+    modes = torch.from_numpy(modes_np).cuda()
+    ranges = torch.empty(2 * H * nq * 4, dtype=torch.int32, device="cuda")
+    order = torch.empty(2 * H, dtype=torch.int32, device="cuda")
+    svg.svg_build_blocks(g, modes, BM, BN, ranges, order)
+    torch.cuda.synchronize()
+    r = ranges.cpu().numpy().reshape(2 * H, nq * 4)
+    og = ogeom(g)
+    work = []
+    for bh in range(2 * H):
+        got = block_bitmap_from_ranges(r[bh], nq, nk)
+        want = oracle.blocks(og, int(modes_np[bh]), BM, BN, brute=L <= 400)
+        assert np.array_equal(got, want), (bh, modes_np[bh])
+        work.append(int(want.sum()))
+    assert np.array_equal(order.cpu().numpy(), oracle.head_order(np.array(work)))
+
+
+def run_attention(g, q, k, v, modes_np, out_dtype, virtual):
+    """Tile lists + (explicit or virtual) layout transformation + attention."""
+    din = svg.BF16 if q.dtype == torch.bfloat16 else svg.F32
+    BM, BN = svg.svg_tile_config(din, g.d)
+    BH = g.B * g.H
+    nq = -(-g.L // BM)
+    modes = torch.from_numpy(np.asarray(modes_np, dtype=np.int32)).cuda()
+    ranges = torch.empty(BH * nq * 4, dtype=torch.int32, device="cuda")
+    order = torch.empty(BH, dtype=torch.int32, device="cuda")
+    svg.svg_build_blocks(g, modes, BM, BN, ranges, order)
+    o = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    if virtual:
+        svg.svg_sparse_attention(g, q, k, v, o, modes, ranges, order, flags=svg.VIRTUAL_PERMUTE)
+    else:
+        qp, kp, vp = (torch.empty_like(t) for t in (q, k, v))
+        for s_, d_ in ((q, qp), (k, kp), (v, vp)):
+            svg.svg_layout_permute(g, s_, d_, modes=modes)
+        op = torch.empty(q.shape, dtype=out_dtype, device="cuda")
+        svg.svg_sparse_attention(g, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op)
+        svg.svg_layout_permute(g, op, o, modes=modes, inverse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy()
+
+
+ATT_CASES = [
+    # dtype, N, F, T, d, a1, a2, window, stripe
+    ("bf16", 5, 100, 0, 128, 2, 12, 100, 130),
+    ("bf16", 3, 77, 13, 64, 1, 9, 30, 64),
+    ("bf16", 9, 40, 5, 128, 3, 6, 50, 70),
+    ("f32", 4, 64, 0, 64, 1, 8, 64, 40),
+    ("f32", 3, 50, 7, 128, 2, 5, 20, 33),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES)
+@pytest.mark.parametrize("virtual", [False, True])
+def test_attention_all_modes(case, virtual):
+    dt, N, F, T, d, a1, a2, W, St = case
+    H = 6
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2, window=W, stripe=St)
+    kinds = [planted_kind(m) for m in MODES6]
+    inp = S.small_config(N, F, T, H, d, a1, a2, kinds, seed=N + F + d, dtype=dt, window=W, stripe=St)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q, k, v = (to_device(inp[n][None], tdt) for n in "qkv")
+    outs = [tdt] if dt == "f32" else [torch.bfloat16, torch.float32]
+    og = ogeom(g)
+    rows = np.arange(g.L)
+    for od in outs:
+        got = run_attention(g, q, k, v, MODES6, od, virtual)
+        for h, mode in enumerate(MODES6):
+            ref = oracle.attention_rows(og, mode, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows)
+            check_close(got[0, h], ref, dt, what=f"mode {mode} out {od}")
+
+
+def test_virtual_equals_explicit_and_deterministic():
+    N, F, T, d = 6, 90, 10, 128
+    g = svg.Geom(B=1, H=6, d=d, N=N, F=F, T=T, a1=2, a2=10, window=45, stripe=100)
+    kinds = [planted_kind(m) for m in MODES6]
+    inp = S.small_config(N, F, T, 6, d, 2, 10, kinds, seed=77, window=45, stripe=100)
+    q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
+    a = run_attention(g, q, k, v, MODES6, torch.bfloat16, False)
+    b = run_attention(g, q, k, v, MODES6, torch.bfloat16, True)
+    c = run_attention(g, q, k, v, MODES6, torch.bfloat16, True)
+    assert np.array_equal(a, b)
+    assert np.array_equal(b, c)
+
+
+@pytest.mark.parametrize("dt,N,F,T,d,a1,a2", [
+    ("bf16", 6, 96, 0, 128, 2, 12), ("bf16", 5, 120, 20, 64, 1, 20), ("f32", 4, 64, 0, 64, 1, 8),
+    ("bf16", 4, 50, 9, 128, 2, 7)])
+def test_profile_labels_bit_exact(dt, N, F, T, d, a1, a2):
+    kinds = [S.SPATIAL, S.TEMPORAL, S.UNSTRUCTURED, S.TEMPORAL, S.SPATIAL, S.UNSTRUCTURED]
+    H = len(kinds)
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2)
+    inp = S.small_config(N, F, T, H, d, a1, a2, kinds, seed=5 * N + d, dtype=dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q, k, v = (to_device(inp[n][None], tdt) for n in "qkv")
+    rows_np = S.sample_rows(N, F, T, 0.15, 3)
+    rows = torch.from_numpy(rows_np).cuda()
+    labels = torch.empty(H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(H * 3, dtype=torch.float32, device="cuda")
+    din = svg.BF16 if dt == "bf16" else svg.F32
+    ws = svg.alloc_workspace(g, din, rows.numel(), svg.VIRTUAL_PERMUTE)
+    svg.svg_profile_heads(g, q, k, v, rows, labels, stats, ws)
+    torch.cuda.synchronize()
+    lab = labels.cpu().numpy()
+    st = stats.cpu().numpy().reshape(H, 3)
+    og = ogeom(g)
+    for h in range(H):
+        want, ref = oracle.profile_head(og, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows_np)
+        assert lab[h] == want, (h, lab[h], want, st[h], ref)
+        # statistics: relative errors to 2 % (absolute floor 1e-4 for near-zero errors)
+        np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
