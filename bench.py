@@ -1,0 +1,262 @@
+"""Benchmark of one Sparse VideoGen attention layer on one MI355X.
+
+A step is one pass of the whole path over the resident inputs of one layer:
+online profiling on 1 % sampled rows -> key-tile lists -> token-major layout
+transformation of the temporal heads' Q, K, V -> block-banded sparse
+attention -> inverse transformation of their output.  Default workload: the
+HunyuanVideo-shaped layer (33 frames x 3600 tokens = 118,800 tokens, 24 heads,
+d = 128, bf16, a1 = 2, a2 = 160).
+
+Prints one JSON line.  ``value`` is the effective throughput of the whole
+step, 4*d*(active query-key pairs) / step time, in TFLOP/s; ``attn_*`` fields
+give the sparse-attention kernel alone (the a5 figure), measured with HIP
+events on the stream the kernels run on.
+
+  python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+                  [--virtual] [--calib-copy]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def pair_count(N, F, T, mode, a1=1, a2=1, window=1, stripe=1):
+    """Active (query, key) pairs of one head, from the masks' closed forms.
+
+    Video-video pairs: spatial F^2 (N + 2 sum_{k=1}^{a1-1} (N-k)), temporal
+    N^2 (F + 2 sum_{k=1}^{a2-1} (F-k)) (thresholds clipped to N, F), window
+    n(2W-1) - W(W-1) for W < n = N*F, stripe n*min(S, n), full n^2; plus the
+    dense text rows and columns T*L + n*T; skip heads have none."""
+    SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
+    n = N * F
+    L = T + n
+    if mode == SKIP:
+        return 0
+    text = T * L + n * T
+    if mode == SPATIAL:
+        a = min(a1, N)
+        vid = F * F * (N + 2 * sum(N - k for k in range(1, a)))
+    elif mode == TEMPORAL:
+        a = min(a2, F)
+        vid = N * N * (F + 2 * sum(F - k for k in range(1, a)))
+    elif mode == FULL:
+        vid = n * n
+    elif mode == WINDOW:
+        W = min(window, n)
+        vid = n * (2 * W - 1) - W * (W - 1)
+    elif mode == STRIPE:
+        vid = n * min(stripe, n)
+    else:
+        raise ValueError(mode)
+    return text + vid
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, inp, labels, d, scale, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    masked attention of seeded query rows of two heads (one per label kind
+    present), timed on the host cores; reported in TFLOP/s of the same
+    4*d*pairs accounting."""
+    import numpy as np
+
+    import oracle
+    c = cfg
+    og = oracle.geom(c["N"], c["F"], c["T"], c["a1"], c["a2"], c.get("window", c["F"]), c.get("stripe", 512))
+    heads = []
+    for want in sorted(set(int(x) for x in labels)):
+        if want == 3:
+            continue
+        heads.append(int(np.nonzero(labels == want)[0][0]))
+    heads = heads[:2]
+    rng = np.random.default_rng(99)
+    L = c["T"] + c["N"] * c["F"]
+    flops = 0.0
+    elapsed = 0.0
+    rows_done = 0
+    n = 8
+    while elapsed < budget_s and n <= L:
+        for h in heads:
+            rows = np.sort(rng.choice(L, size=n, replace=False)).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.attention_rows(og, int(labels[h]), inp["q"][h], inp["k"][h], inp["v"][h], scale, rows)
+            elapsed += time.perf_counter() - t0
+            for r in rows:
+                iv = oracle.row_intervals(og, oracle.TEMPORAL if labels[h] == 1 else int(labels[h]), int(r))
+                flops += 4.0 * d * sum(hi - lo for lo, hi in iv)
+            rows_done += n
+        n *= 2
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows_done} seeded query rows of heads {heads} (labels "
+                      f"{[int(labels[h]) for h in heads]}), fp64 oracle masked attention, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--call", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--virtual", action="store_true",
+                    help="temporal heads gather through the index map instead of explicit permutes")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by head with no "
+              "cross-GPU exchange, and multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_video_svg_amd as svg
+    import svg_synth as S
+
+    cfg = S.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = S.make_inputs(args.config, call=args.call)
+    log(f"inputs for config {args.config} generated in {time.time() - t0:.1f} s")
+    bf16 = cfg["dtype"] == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    din = svg.BF16 if bf16 else svg.F32
+    geom = svg.Geom(B=1, H=cfg["H"], d=cfg["d"], N=cfg["N"], F=cfg["F"], T=cfg["T"], a1=cfg["a1"], a2=cfg["a2"],
+                    window=cfg.get("window", cfg["F"]), stripe=cfg.get("stripe", 512))
+    H, d, L = geom.H, geom.d, geom.L
+    q = torch.from_numpy(inp["q"]).to(dev).to(tdt)[None]
+    k = torch.from_numpy(inp["k"]).to(dev).to(tdt)[None]
+    v = torch.from_numpy(inp["v"]).to(dev).to(tdt)[None]
+    o = torch.empty_like(q)
+    profile = inp["rows"] is not None
+    rows = torch.from_numpy(inp["rows"]).to(dev) if profile else None
+    n_rows = 0 if rows is None else rows.numel()
+    BM, BN = svg.svg_tile_config(din, d)
+    nQT = -(-L // BM)
+    labels = torch.empty(H, dtype=torch.int32, device=dev)
+    stats = torch.empty(H * 3, dtype=torch.float32, device=dev)
+    ranges = torch.empty(H * nQT * 4, dtype=torch.int32, device=dev)
+    order = torch.empty(H, dtype=torch.int32, device=dev)
+    ws = svg.alloc_workspace(geom, din, n_rows, svg.VIRTUAL_PERMUTE)
+    flags = svg.VIRTUAL_PERMUTE if args.virtual else 0
+    if not args.virtual:
+        qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
+    else:
+        qp = kp = vp = op = None
+    modes_fixed = None if profile else torch.from_numpy(inp["kinds"].astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks):
+        """One layer; records an event after each stage into marks (list)."""
+        marks.append(ev()); marks[-1].record(stream)
+        if profile:
+            svg.svg_profile_heads(geom, q, k, v, rows, labels, stats, ws)
+            modes = labels
+        else:
+            modes = modes_fixed
+        marks.append(ev()); marks[-1].record(stream)
+        svg.svg_build_blocks(geom, modes, BM, BN, ranges, order)
+        marks.append(ev()); marks[-1].record(stream)
+        if not args.virtual:
+            for s_, d_ in ((q, qp), (k, kp), (v, vp)):
+                svg.svg_layout_permute(geom, s_, d_, modes=modes)
+        marks.append(ev()); marks[-1].record(stream)
+        svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op, flags=flags)
+        marks.append(ev()); marks[-1].record(stream)
+        if not args.virtual:
+            svg.svg_layout_permute(geom, op, o, modes=modes, inverse=True)
+        marks.append(ev()); marks[-1].record(stream)
+
+    for i in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    all_marks = []
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        m = []
+        step(m)
+        all_marks.append(m)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stage = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(5)] for m in all_marks])
+    prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage.mean(axis=0)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    lab = labels.cpu().numpy() if profile else inp["kinds"].astype(np.int32)
+    pairs = [pair_count(geom.N, geom.F, geom.T, int(m), geom.a1, geom.a2, geom.window, geom.stripe) for m in lab]
+    flops = 4.0 * d * float(sum(pairs))
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    n_temporal = int((lab == 1).sum())
+    elt = 2 if bf16 else 4
+    perm_bytes = 2.0 * n_temporal * L * d * elt  # read + write per permuted head-tensor
+    fwd_gbs = 3 * perm_bytes / (perm_ms * 1e-3) / 1e9 if perm_ms > 0 and n_temporal else None
+    inv_gbs = perm_bytes / (inv_ms * 1e-3) / 1e9 if inv_ms > 0 and n_temporal else None
+    result = {
+        "metric": "sparse-attn ms/layer + effective TFLOP/s vs bf16 MFMA peak (33x3600x24h x d128)",
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded planted Q/K/V, no model activations)",
+        "config": {"workload": f"{cfg['name']} (config {args.config})", "frames": geom.N,
+                   "tokens_per_frame": geom.F, "text_tokens": geom.T, "heads": H, "head_dim": d,
+                   "a1": geom.a1, "a2": geom.a2, "sampled_rows": n_rows, "layout": "virtual" if args.virtual
+                   else "explicit", "labels": {"spatial": int((lab == 0).sum()), "temporal": n_temporal,
+                                               "full": int((lab == 2).sum()), "other": int((lab > 2).sum())}},
+        "attn_ms": round(float(attn_ms), 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_of_peak": round(attn_tflops / peak, 4),
+        "profile_ms": round(float(prof_ms), 4),
+        "blocks_ms": round(float(blocks_ms), 4),
+        "permute_fwd_ms": round(float(perm_ms), 4),
+        "permute_inv_ms": round(float(inv_ms), 4),
+        "permute_fwd_gbs": None if fwd_gbs is None else round(fwd_gbs, 1),
+        "permute_inv_gbs": None if inv_gbs is None else round(inv_gbs, 1),
+        "effective_flops_per_layer": flops,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "kernel": "k_attn_bf16 (svg_sparse_attention)" if bf16 else "k_attn_f32"},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, lab, d, 1.0 / np.sqrt(d))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,11 +11,11 @@ a head of a given kind shares a per-frame vector (spatial-like), a
 per-position vector (temporal-like) or a global vector (stripe-like) between
 its queries and keys, plus independent Gaussian noise; values are iid N(0,1).
 
-Random-number recipe (numpy PCG64, fixed draw order):
-  rng = default_rng(1000 * config + call)
-  1. head kinds / modes (when drawn), 2. for each head in order: planted
-  vectors, query noise [L, d], key noise [L, d], values [L, d];
-  sampled rows come from default_rng(1000 * config + call + 500).
+Random-number recipe (numpy PCG64, fixed draw order), seed = 1000*config + call:
+  head kinds / modes (when drawn) from default_rng(seed);
+  head h from its own stream default_rng([seed, h + 1]): planted vectors,
+  then query noise [L, d], key noise [L, d], values [L, d];
+  sampled rows from default_rng(seed + 500).
 Values are rounded to bf16 (round-to-nearest-even) for the bf16 workloads;
 both sides receive the same bits.
 """
@@ -107,39 +107,43 @@ def _plant(kind, cfg, c, rng, L):
     return sig_q, sig_k
 
 
-def make_inputs(cfg, call=0, heads=None):
+def _head(cfg, c, kind, seed, h, L):
+    rng = np.random.default_rng([seed, h + 1])
+    sig_q, sig_k = _plant(kind, cfg, c, rng, L)
+    d = c["d"]
+    q = sig_q + c["noise"] * rng.standard_normal((L, d), dtype=np.float32)
+    k = sig_k + c["noise"] * rng.standard_normal((L, d), dtype=np.float32)
+    v = rng.standard_normal((L, d), dtype=np.float32)
+    if c["dtype"] == "bf16":
+        q, k, v = (bf16_to_f32(bf16_bits(a)) for a in (q, k, v))
+    return q, k, v
+
+
+def make_inputs(cfg, call=0, heads=None, workers=8):
     """Inputs of one workload call.
 
-    Returns dict with q, k, v as float32 arrays [H, L, d] holding exactly the
-    values both sides use (bf16-representable for bf16 workloads), the head
-    kinds, the sampled rows, the seed and the config dict.  ``heads`` limits
-    which heads are materialised (others are still drawn, to keep streams
-    aligned, but not stored); stored arrays are then [len(heads), L, d].
+    Returns dict with q, k, v as float32 arrays [len(heads), L, d] holding
+    exactly the values both sides use (bf16-representable for bf16
+    workloads), the head kinds of all heads, the sampled rows, the seed and
+    the config dict.  ``heads`` selects which heads are materialised (every
+    head has its own random stream, so a subset is drawn identically).
     """
+    import concurrent.futures
     c = CONFIGS[cfg]
     N, F, T, H, d = c["N"], c["F"], c["T"], c["H"], c["d"]
     L = T + N * F
     seed = 1000 * cfg + call
-    rng = np.random.default_rng(seed)
-    kinds = head_kinds(cfg, rng)
+    kinds = head_kinds(cfg, np.random.default_rng(seed))
     keep = list(range(H)) if heads is None else list(heads)
     q = np.empty((len(keep), L, d), dtype=np.float32)
     k = np.empty_like(q)
     v = np.empty_like(q)
-    slot = {h: i for i, h in enumerate(keep)}
-    for h in range(H):
-        sig_q, sig_k = _plant(kinds[h], cfg, c, rng, L)
-        nq = rng.standard_normal((L, d), dtype=np.float32)
-        nk = rng.standard_normal((L, d), dtype=np.float32)
-        nv = rng.standard_normal((L, d), dtype=np.float32)
-        if h not in slot:
-            continue
-        i = slot[h]
-        q[i] = sig_q + c["noise"] * nq
-        k[i] = sig_k + c["noise"] * nk
-        v[i] = nv
-    if c["dtype"] == "bf16":
-        q, k, v = (bf16_to_f32(bf16_bits(a)) for a in (q, k, v))
+
+    def fill(i):
+        q[i], k[i], v[i] = _head(cfg, c, kinds[keep[i]], seed, keep[i], L)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(len(keep))))
     rows = None
     if c["sample"] is not None:
         rows = sample_rows(N, F, T, c["sample"], seed + 500)
