@@ -125,6 +125,116 @@ __device__ __forceinline__ int acc_key(int kb2, int r, int hh) {
   return kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+// Online-softmax state of one output (per lane: one query, the dims of the
+// accumulator layout).  m_ref is the running reference max in log2 units; it
+// only moves when a lane's tile max exceeds it by more than 2^kRescaleTau, and
+// that decision is per lane, so a row's result never depends on which other
+// rows share its wave.
+template <int D>
+struct Flash {
+  f32x16 o[D / 32];
+  float m_ref, l_part;
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    m_ref = -INFINITY;
+    l_part = 0.f;
+  }
+
+  // s0, s1: raw scores of the two 32-key blocks of a tile, masked entries
+  // already -inf.  sl2 = scale * log2(e) > 0.
+  __device__ __forceinline__ void add_tile(const f32x16& s0, const f32x16& s1, const __bf16* lv, int lane,
+                                           float sl2) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = half_max(mx) * sl2;
+    const bool need = mx > m_ref + kRescaleTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // lanes with nothing accumulated yet (m_ref = -inf) hold o = l = 0
+      const float alpha = !need ? 1.f : (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx));
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      m_ref = need ? mx : m_ref;
+    }
+    const float nmu = m_ref == -INFINITY ? 0.f : -m_ref;
+#pragma unroll
+    for (int s16 = 0; s16 < 4; ++s16) {
+      f32x8 p8;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float sv = (s16 >> 1) ? s1[(s16 & 1) * 8 + r] : s0[(s16 & 1) * 8 + r];
+        p8[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sl2, nmu));
+        l_part += p8[r];
+      }
+      const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// Mask the raw scores of a tile to the lane's active keys [0, T) U [lo, hi).
+__device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt0, int hh, int T, int lo, int hi) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int k0 = kt0 + acc_key(0, r, hh), k1 = kt0 + acc_key(1, r, hh);
+    if (!(k0 < T || (k0 >= lo && k0 < hi))) s0[r] = -INFINITY;
+    if (!(k1 < T || (k1 >= lo && k1 < hi))) s1[r] = -INFINITY;
+  }
+}
+
+// Single-output flash sweep of a workgroup over a tile sequence given as two
+// ranges [rg.x, rg.y) U [rg.z, rg.w) of key tiles.  Every lane's active keys
+// are [0, T) U [lo, hi); `valid` marks lanes with a real query row.  The
+// caller has already issued the loads of the first tile into buffer 0.
+template <int D, typename RowMap>
+__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const __bf16* K, const __bf16* V, int64_t sx,
+                                      RowMap phys, int4 rg, int L, int T, int lo, int hi, bool valid, float sl2,
+                                      __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+  const int hh = lane >> 5;
+  const int n1 = rg.y - rg.x, nt = n1 + (rg.w - rg.z);
+  auto tile_of = [&](int t) { return t < n1 ? rg.x + t : rg.z + (t - n1); };
+  // wave-wide run bounds over valid rows: a tile is full for the wave when it
+  // lies in every row's run, idle when it lies outside all of them
+  const int max_lo = wave_max_i(valid ? lo : INT_MIN);
+  const int min_hi = wave_min_i(valid ? hi : INT_MAX);
+  const int min_lo = wave_min_i(valid ? lo : INT_MAX);
+  const int max_hi = wave_max_i(valid ? hi : INT_MIN);
+  const bool wave_rows = wave_max_i(valid ? 1 : 0) != 0;
+  st.init();
+  wait_vm_all();
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    const int bf = t & 1;
+    if (t + 1 < nt) load_kv_tile<D>(K, V, sx, tile_of(t + 1) * kBN, L, phys, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
+    const int kt0 = tile_of(t) * kBN, kt1 = kt0 + kBN;
+    const bool idle = kt0 >= T && (kt1 <= min_lo || kt0 >= max_hi);
+    if (wave_rows && !idle) {
+      const bool full = (kt1 <= T) || (max(kt0, T) >= max_lo && kt1 <= min_hi);
+      const __bf16* lk = lds[bf][0];
+      f32x16 s0 = score_block<D>(lk, qf, 0, lane);
+      f32x16 s1 = score_block<D>(lk, qf, 1, lane);
+      if (!full) mask_tile(s0, s1, kt0, hh, T, lo, hi);
+      st.add_tile(s0, s1, lds[bf][1], lane, sl2);
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int hh) {
+  const __bf16* qrow = qrow_base + 8 * hh;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+}
+
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT, int32_t total) {
   using C = TileCfg<D>;
@@ -167,108 +277,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
   }
 
   const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
-  const int n1 = rg.y - rg.x, nt = n1 + (rg.w - rg.z);
-  auto tile_of = [&](int t) { return t < n1 ? rg.x + t : rg.z + (t - n1); };
-
-  if (nt > 0) load_kv_tile<D>(K, V, sin.x, tile_of(0) * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
+  if (rg.y > rg.x) load_kv_tile<D>(K, V, sin.x, rg.x * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
+  else if (rg.w > rg.z) load_kv_tile<D>(K, V, sin.x, rg.z * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
 
   // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
   const int xq = row0 + wave * 32 + (lane & 31);
   const bool valid = xq < g.L;
   const int xqc = valid ? xq : g.L - 1;
   bf16x8 qf[D / 16];
-  {
-    const __bf16* qrow = Q + (int64_t)phys(xqc) * sin.x + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-  }
+  load_q<D>(qf, Q + (int64_t)phys(xqc) * sin.x, hh);
   int lo, hi;
   row_interval(g, mode, xqc, lo, hi);
-  // wave-wide run bounds over valid rows: a tile is full for the wave when it
-  // lies in every row's run, idle when it lies outside all of them
-  const int max_lo = wave_max_i(valid ? lo : INT_MIN);
-  const int min_hi = wave_min_i(valid ? hi : INT_MAX);
-  const int min_lo = wave_min_i(valid ? lo : INT_MAX);
-  const int max_hi = wave_max_i(valid ? hi : INT_MIN);
-  const bool wave_rows = wave_max_i(valid ? 1 : 0) != 0;
 
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_ref = -INFINITY, l_part = 0.f;
-  const float sl2 = g.scale_log2;
-
-  wait_vm_all();
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    const int bf = t & 1;
-    if (t + 1 < nt)
-      load_kv_tile<D>(K, V, sin.x, tile_of(t + 1) * kBN, g.L, phys, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
-    const int kt0 = tile_of(t) * kBN, kt1 = kt0 + kBN;
-    const bool idle = kt0 >= g.T && (kt1 <= min_lo || kt0 >= max_hi);
-    if (wave_rows && !idle) {
-      const bool full = (kt1 <= g.T) || (max(kt0, g.T) >= max_lo && kt1 <= min_hi);
-      const __bf16* lk = lds[bf][0];
-      const __bf16* lv = lds[bf][1];
-      f32x16 s0 = score_block<D>(lk, qf, 0, lane);
-      f32x16 s1 = score_block<D>(lk, qf, 1, lane);
-      float mx = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] *= sl2;
-          s1[r] *= sl2;
-          mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int k0 = kt0 + acc_key(0, r, hh), k1 = kt0 + acc_key(1, r, hh);
-          const bool a0 = k0 < g.T || (k0 >= lo && k0 < hi);
-          const bool a1 = k1 < g.T || (k1 >= lo && k1 < hi);
-          s0[r] = a0 ? s0[r] * sl2 : -INFINITY;
-          s1[r] = a1 ? s1[r] * sl2 : -INFINITY;
-          mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        }
-      }
-      mx = half_max(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleTau) != 0) {
-        const float mn = fmaxf(m_ref, mx);
-        // rows with nothing accumulated yet have o = l = 0 (and may still have mn = -inf)
-        const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        m_ref = mn;
-      }
-      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-      f32x8 p8[4];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p8[0][r] = __builtin_amdgcn_exp2f(s0[r] - mu);
-        p8[1][r] = __builtin_amdgcn_exp2f(s0[r + 8] - mu);
-        p8[2][r] = __builtin_amdgcn_exp2f(s1[r] - mu);
-        p8[3][r] = __builtin_amdgcn_exp2f(s1[r + 8] - mu);
-      }
-#pragma unroll
-      for (int s16 = 0; s16 < 4; ++s16) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) l_part += p8[s16][r];
-        const bf16x8 pb = __builtin_convertvector(p8[s16], bf16x8);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
-        }
-      }
-    }
-    wait_vm_all();
-    __syncthreads();
-  }
+  Flash<D> st;
+  sweep<D>(st, qf, K, V, sin.x, phys, rg, g.L, g.T, lo, hi, valid, g.scale_log2, lds, wave, lane);
 
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
-  const float l_tot = half_sum(l_part);
+  const float l_tot = half_sum(st.l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (valid) {
     char* orow = O + (obase + (int64_t)phys(xq) * sout.x) * OE;
@@ -277,7 +302,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * hh;
-        f32x4 v4 = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
+        f32x4 v4 = {st.o[db][4 * g4] * inv, st.o[db][4 * g4 + 1] * inv, st.o[db][4 * g4 + 2] * inv,
+                    st.o[db][4 * g4 + 3] * inv};
         if (OUT_BF16) {
           bf16x4 b4 = __builtin_convertvector(v4, bf16x4);
           *reinterpret_cast<bf16x4*>(orow + d0 * 2) = b4;
@@ -289,32 +315,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
   }
 }
 
-// ---------------------------------------------------------------------------
-// Profiling sweep (bf16): every workgroup takes 128 sampled rows of one head
-// (4 waves x 32) and one of `ksplit` slices of the key tiles, and keeps three
-// online-softmax states per row: full attention, the spatial mask and the
-// temporal mask (mod form, frame-major order).  It writes each state's
-// (m, l, acc) for the merge kernel.  The scores and the V fragments of a tile
-// are shared by the three states.
-
-// Tile-relative active key offsets [a0, b0) U [a1, b1) of one state.
-struct Runs {
-  int a0, b0, a1, b1;
-};
-// Clip [a0, b0) U [a1, b1) to the tile; empty runs become [a, a).
-__device__ __forceinline__ Runs make_runs(int a0, int b0, int a1, int b1, int n) {
-  a0 = min(max(a0, 0), n);
-  b0 = min(max(b0, a0), n);
-  a1 = min(max(a1, 0), n);
-  b1 = min(max(b1, a1), n);
-  return Runs{a0, b0, a1, b1};
-}
-__device__ __forceinline__ bool in_runs(const Runs& r, int e) {
-  return (unsigned)(e - r.a0) < (unsigned)(r.b0 - r.a0) || (unsigned)(e - r.a1) < (unsigned)(r.b1 - r.a1);
-}
-
+// Partial (m, l, acc) of one output of one sampled row: acc in the
+// accumulator layout order is written back to dims order.
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_profile_bf16(KGeom g, const __bf16* __restrict__ q,
+__device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, float* ml, int hh) {
+  const float l_tot = half_sum(st.l_part);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = db * 32 + 8 * g4 + 4 * hh;
+      *reinterpret_cast<f32x4*>(acc + d0) =
+          f32x4{st.o[db][4 * g4], st.o[db][4 * g4 + 1], st.o[db][4 * g4 + 2], st.o[db][4 * g4 + 3]};
+    }
+  if (hh == 0) {
+    ml[0] = st.m_ref;
+    ml[1] = l_tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Profiling, sweep 1 (frame-major keys): full and spatial attention of the
+// sampled rows.  Each key goes to exactly one of two online-softmax states,
+// IN (the row's spatial keys: its frame run and the text prefix) and OUT (all
+// other keys), so the tile's P.V is computed once; the merge then gives
+// O_spatial = IN and O_full = IN combined with OUT.  A workgroup takes 128
+// sampled rows (4 waves x 32) of one head and one of `ksplit` slices of the
+// key tiles.
+template <int D>
+__global__ __launch_bounds__(256, 1) void k_prof_spatial(KGeom g, const __bf16* __restrict__ q,
                                                          const __bf16* __restrict__ k,
                                                          const __bf16* __restrict__ v, svg_strides s,
                                                          const int32_t* __restrict__ rows, int32_t n_rows,
@@ -326,7 +355,6 @@ __global__ __launch_bounds__(256, 1) void k_profile_bf16(KGeom g, const __bf16* 
   const int chunk = blockIdx.x, split = blockIdx.y, bh = blockIdx.z;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  const __bf16* Q = q + base;
   const __bf16* K = k + base;
   const __bf16* V = v + base;
   auto ident = [](int r) { return r; };
@@ -340,152 +368,117 @@ __global__ __launch_bounds__(256, 1) void k_profile_bf16(KGeom g, const __bf16* 
   const bool valid = ridx < n_rows;
   const int x = rows[valid ? ridx : n_rows - 1];
   bf16x8 qf[D / 16];
-  {
-    const __bf16* qrow = Q + (int64_t)x * s.x + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-  }
-  // spatial run [slo, shi) of whole frames; temporal positions [jlo, jhi)
+  load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
+  // spatial run [slo, shi) of whole frames (text keys are IN as well)
   const int u = x - g.T;
-  const int fi = fastdiv(u, g.divF_mul, g.divF_shift), fj = u - fi * g.F;
+  const int fi = fastdiv(u, g.divF_mul, g.divF_shift);
   const int slo = g.T + max(0, fi - g.a1 + 1) * g.F, shi = g.T + min(g.N, fi + g.a1) * g.F;
-  const int jlo = max(0, fj - g.a2 + 1), jhi = min(g.F, fj + g.a2);
-  const int w_slo = wave_min_i(valid ? slo : INT_MAX), w_shi = wave_max_i(valid ? shi : INT_MIN);
-
-  f32x16 o[3][D / 32];
-#pragma unroll
-  for (int st = 0; st < 3; ++st)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[st][db] = f32x16{};
-  float m_ref[3] = {-INFINITY, -INFINITY, -INFINITY}, l_part[3] = {0.f, 0.f, 0.f};
+  const int max_slo = wave_max_i(valid ? slo : INT_MIN), min_shi = wave_min_i(valid ? shi : INT_MAX);
+  const int min_slo = wave_min_i(valid ? slo : INT_MAX), max_shi = wave_max_i(valid ? shi : INT_MIN);
   const float sl2 = g.scale_log2;
 
+  Flash<D> in_st, out_st;
+  in_st.init();
+  out_st.init();
   wait_vm_all();
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     const int bf = t & 1;
     if (t + 1 < nt)
       load_kv_tile<D>(K, V, s.x, (t_begin + t + 1) * kBN, g.L, ident, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
-    const int kt0 = (t_begin + t) * kBN;
+    const int kt0 = (t_begin + t) * kBN, kt1 = kt0 + kBN;
     const __bf16* lk = lds[bf][0];
     const __bf16* lv = lds[bf][1];
-    const int nvalid = min(kBN, g.L - kt0);
-    const int ntext = max(0, min(kBN, g.T - kt0));
-    // active runs of each state, tile-relative
-    Runs run[3];
-    run[0] = make_runs(0, nvalid, 0, 0, nvalid);
-    run[1] = make_runs(0, ntext, slo - kt0, shi - kt0, nvalid);
-    const bool tp_simple = kt0 >= g.T && g.F >= kBN;
-    if (tp_simple) {  // positions of the tile wrap at most once
-      const int uk = kt0 - g.T;
-      const int jt0 = uk - fastdiv(uk, g.divF_mul, g.divF_shift) * g.F;
-      run[2] = make_runs(jlo - jt0, jhi - jt0, jlo - jt0 + g.F, jhi - jt0 + g.F, nvalid);
+    f32x16 s0 = score_block<D>(lk, qf, 0, lane);
+    f32x16 s1 = score_block<D>(lk, qf, 1, lane);
+    const bool all_in = kt1 <= g.T || (kt0 >= max_slo && kt1 <= min_shi);
+    const bool all_out = kt0 >= g.T && kt1 <= g.L && (kt1 <= min_slo || kt0 >= max_shi);
+    if (all_in) {
+      in_st.add_tile(s0, s1, lv, lane, sl2);
+    } else if (all_out) {
+      out_st.add_tile(s0, s1, lv, lane, sl2);
     } else {
-      run[2] = Runs{0, 0, 0, 0};
-    }
-    f32x16 sc0 = score_block<D>(lk, qf, 0, lane);
-    f32x16 sc1 = score_block<D>(lk, qf, 1, lane);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc0[r] *= sl2;
-      sc1[r] *= sl2;
-    }
-    // Softmax of one state into bf16 P fragments (masked keys give p = 0, so a
-    // state with no active key in the tile contributes nothing).
-    auto state_p = [&](int st, bf16x8* pb) {
-      f32x16 z0, z1;
-      float mx = -INFINITY;
+      f32x16 i0 = s0, i1 = s1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int e0 = acc_key(0, r, hh), e1 = acc_key(1, r, hh);
-        bool a0, a1;
-        if (st == 2 && !tp_simple) {  // general path: text keys and short frames
-          const int k0 = kt0 + e0, k1 = kt0 + e1;
-          const int u0 = k0 - g.T, u1 = k1 - g.T;
-          const int j0 = u0 - fastdiv(max(u0, 0), g.divF_mul, g.divF_shift) * g.F;
-          const int j1 = u1 - fastdiv(max(u1, 0), g.divF_mul, g.divF_shift) * g.F;
-          a0 = e0 < nvalid && (k0 < g.T || (j0 >= jlo && j0 < jhi));
-          a1 = e1 < nvalid && (k1 < g.T || (j1 >= jlo && j1 < jhi));
-        } else {
-          a0 = in_runs(run[st], e0);
-          a1 = in_runs(run[st], e1);
-        }
-        z0[r] = a0 ? sc0[r] : -INFINITY;
-        z1[r] = a1 ? sc1[r] : -INFINITY;
-        mx = fmaxf(mx, fmaxf(z0[r], z1[r]));
+        const int k0 = kt0 + acc_key(0, r, hh), k1 = kt0 + acc_key(1, r, hh);
+        const bool in0 = k0 < g.T || (k0 >= slo && k0 < shi), in1 = k1 < g.T || (k1 >= slo && k1 < shi);
+        i0[r] = in0 ? s0[r] : -INFINITY;
+        i1[r] = in1 ? s1[r] : -INFINITY;
+        s0[r] = (in0 || k0 >= g.L) ? -INFINITY : s0[r];
+        s1[r] = (in1 || k1 >= g.L) ? -INFINITY : s1[r];
       }
-      mx = half_max(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref[st] + kRescaleTau) != 0) {
-        const float mn = fmaxf(m_ref[st], mx);
-        const float alpha = m_ref[st] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[st] - mn);
-        l_part[st] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[st][db] *= alpha;
-        m_ref[st] = mn;
-      }
-      const float mu = m_ref[st] == -INFINITY ? 0.f : m_ref[st];
-#pragma unroll
-      for (int s16 = 0; s16 < 4; ++s16) {
-        f32x8 p8;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float zz = (s16 >> 1) ? z1[(s16 & 1) * 8 + r] : z0[(s16 & 1) * 8 + r];
-          p8[r] = __builtin_amdgcn_exp2f(zz - mu);
-          l_part[st] += p8[r];
-        }
-        pb[s16] = __builtin_convertvector(p8, bf16x8);
-      }
-    };
-    // full and temporal states: every tile
-    {
-      bf16x8 pf[4], pt[4];
-      state_p(0, pf);
-      state_p(2, pt);
-#pragma unroll
-      for (int s16 = 0; s16 < 4; ++s16) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
-          o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s16], o[0][db], 0, 0, 0);
-          o[2][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pt[s16], o[2][db], 0, 0, 0);
-        }
-      }
-    }
-    // spatial state: only tiles with text keys or inside the wave's frame run
-    if (kt0 < g.T || (kt0 + kBN > w_slo && kt0 < w_shi)) {
-      bf16x8 ps[4];
-      state_p(1, ps);
-#pragma unroll
-      for (int s16 = 0; s16 < 4; ++s16) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
-          o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ps[s16], o[1][db], 0, 0, 0);
-        }
-      }
+      in_st.add_tile(i0, i1, lv, lane, sl2);
+      out_st.add_tile(s0, s1, lv, lane, sl2);
     }
     wait_vm_all();
     __syncthreads();
   }
-  // partial outputs: slot = ((bh * n_rows + ridx) * ksplit + split) * 3 + state
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    const float l_tot = half_sum(l_part[st]);
-    if (!valid) continue;
-    const int64_t slot = (((int64_t)bh * n_rows + ridx) * ksplit + split) * 3 + st;
-    float* acc = part_acc + slot * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hh;
-        *reinterpret_cast<f32x4*>(acc + d0) = f32x4{o[st][db][4 * g4], o[st][db][4 * g4 + 1],
-                                                    o[st][db][4 * g4 + 2], o[st][db][4 * g4 + 3]};
-      }
-    if (hh == 0) {
-      part_ml[slot * 2] = m_ref[st];
-      part_ml[slot * 2 + 1] = l_tot;
-    }
+  if (valid) {
+    const int64_t slot = (((int64_t)bh * n_rows + ridx) * ksplit + split) * 2;
+    store_partial<D>(in_st, part_acc + slot * D, part_ml + slot * 2, hh);
+    store_partial<D>(out_st, part_acc + (slot + 1) * D, part_ml + (slot + 1) * 2, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Profiling, sweep 2 (token-major keys): temporal attention of the sampled
+// rows.  In token-major order a row's temporal keys are one band (plus the
+// text prefix), so with the rows taken in order of their position j (the
+// order from k_prof_rank) a workgroup's 128 rows need only the union of
+// their bands.  K and V rows are gathered through the index map; queries are
+// read in place.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_prof_temporal(KGeom g, const __bf16* __restrict__ q,
+                                                          const __bf16* __restrict__ k,
+                                                          const __bf16* __restrict__ v, svg_strides s,
+                                                          const int32_t* __restrict__ ord_x,
+                                                          const int32_t* __restrict__ ord_r, int32_t n_rows,
+                                                          float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  using C = TileCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];
+  __shared__ int wb[2][4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / g.H, h = bh % g.H;
+  const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
+  const __bf16* K = k + base;
+  const __bf16* V = v + base;
+  const KGeom gg = g;
+  auto phys = [gg](int r) { return perm_inv_row(gg, r); };
+
+  const int rk = chunk * kProfRows_bf16 + wave * 32 + (lane & 31);
+  const bool valid = rk < n_rows;
+  const int x = ord_x[valid ? rk : n_rows - 1];
+  const int u = x - g.T;
+  const int j = u - fastdiv(u, g.divF_mul, g.divF_shift) * g.F;
+  const int lo = g.T + max(0, j - g.a2 + 1) * g.N, hi = g.T + min(g.F, j + g.a2) * g.N;
+  // workgroup's band union -> tile ranges (text tiles first)
+  const int wlo = wave_min_i(valid ? lo : INT_MAX), whi = wave_max_i(valid ? hi : INT_MIN);
+  if (lane == 0) {
+    wb[0][wave] = wlo;
+    wb[1][wave] = whi;
+  }
+  __syncthreads();
+  const int ulo = min(min(wb[0][0], wb[0][1]), min(wb[0][2], wb[0][3]));
+  const int uhi = max(max(wb[1][0], wb[1][1]), max(wb[1][2], wb[1][3]));
+  const int bs = ulo / kBN, be = (uhi + kBN - 1) / kBN, te = (g.T + kBN - 1) / kBN;
+  int4 rg;
+  if (g.T == 0)
+    rg = make_int4(bs, be, 0, 0);
+  else if (te >= bs)
+    rg = make_int4(0, max(be, te), 0, 0);
+  else
+    rg = make_int4(0, te, bs, be);
+  load_kv_tile<D>(K, V, s.x, rg.x * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
+
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
+  Flash<D> st;
+  sweep<D>(st, qf, K, V, s.x, phys, rg, g.L, g.T, lo, hi, valid, g.scale_log2, lds, wave, lane);
+  if (valid) {
+    const int64_t slot = (int64_t)bh * n_rows + ord_r[rk];
+    store_partial<D>(st, part_acc + slot * D, part_ml + slot * 2, hh);
   }
 }
 
@@ -510,17 +503,24 @@ hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf1
 }
 
 hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                               const int32_t* rows, int32_t n_rows, int32_t ksplit, float* part_acc,
-                               float* part_ml, hipStream_t st) {
-  dim3 grid((unsigned)((n_rows + kProfRows_bf16 - 1) / kProfRows_bf16), (unsigned)ksplit, (unsigned)(g.B * g.H));
+                               const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                               const int32_t* ord_r, float* p1_acc, float* p1_ml, float* p2_acc, float* p2_ml,
+                               hipStream_t st) {
+  const unsigned chunks = (unsigned)((n_rows + kProfRows_bf16 - 1) / kProfRows_bf16);
+  const unsigned BH = (unsigned)(g.B * g.H);
   const __bf16 *bq = static_cast<const __bf16*>(q), *bk = static_cast<const __bf16*>(k),
                *bv = static_cast<const __bf16*>(v);
-  if (g.d == 64)
-    hipLaunchKernelGGL(k_profile_bf16<64>, grid, dim3(256), 0, st, g, bq, bk, bv, s, rows, n_rows, ksplit,
-                       part_acc, part_ml);
-  else
-    hipLaunchKernelGGL(k_profile_bf16<128>, grid, dim3(256), 0, st, g, bq, bk, bv, s, rows, n_rows, ksplit,
-                       part_acc, part_ml);
+  if (g.d == 64) {
+    hipLaunchKernelGGL(k_prof_spatial<64>, dim3(chunks, (unsigned)ksplit, BH), dim3(256), 0, st, g, bq, bk, bv, s,
+                       rows, n_rows, ksplit, p1_acc, p1_ml);
+    hipLaunchKernelGGL(k_prof_temporal<64>, dim3(chunks, BH), dim3(256), 0, st, g, bq, bk, bv, s, ord_x, ord_r,
+                       n_rows, p2_acc, p2_ml);
+  } else {
+    hipLaunchKernelGGL(k_prof_spatial<128>, dim3(chunks, (unsigned)ksplit, BH), dim3(256), 0, st, g, bq, bk, bv, s,
+                       rows, n_rows, ksplit, p1_acc, p1_ml);
+    hipLaunchKernelGGL(k_prof_temporal<128>, dim3(chunks, BH), dim3(256), 0, st, g, bq, bk, bv, s, ord_x, ord_r,
+                       n_rows, p2_acc, p2_ml);
+  }
   return hipGetLastError();
 }
 

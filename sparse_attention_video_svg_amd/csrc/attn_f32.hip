@@ -103,8 +103,9 @@ template <int D>
 __global__ __launch_bounds__(64) void k_profile_f32(KGeom g, const float* __restrict__ q,
                                                     const float* __restrict__ k, const float* __restrict__ v,
                                                     svg_strides s, const int32_t* __restrict__ rows,
-                                                    int32_t n_rows, float* __restrict__ part_acc,
-                                                    float* __restrict__ part_ml) {
+                                                    int32_t n_rows, float* __restrict__ p1_acc,
+                                                    float* __restrict__ p1_ml, float* __restrict__ p2_acc,
+                                                    float* __restrict__ p2_ml) {
   __shared__ float qs[D];
   __shared__ double ps[3][64];
   const int lane = threadIdx.x;
@@ -173,17 +174,22 @@ __global__ __launch_bounds__(64) void k_profile_f32(KGeom g, const float* __rest
     }
     __syncthreads();
   }
-  // one split: the partial is already normalised to its own max, so store
-  // (m, l, acc) with acc / l as the output and m in log2 units for the merge
+  // Outputs already normalised (l = 1, m = 0): sweep-1 slots hold the
+  // spatial (state 0) and the full output (state 1, merged with full_direct),
+  // the sweep-2 slot holds the temporal output.
+  const int64_t row = (int64_t)bh * n_rows + r;
+  float* dst_acc[3] = {p1_acc + (row * 2 + 0) * D, p1_acc + (row * 2 + 1) * D, p2_acc + row * D};
+  float* dst_ml[3] = {p1_ml + (row * 2 + 0) * 2, p1_ml + (row * 2 + 1) * 2, p2_ml + row * 2};
+  const int which[3] = {1, 0, 2};  // destination of full, spatial, temporal
 #pragma unroll
   for (int st = 0; st < 3; ++st) {
-    const int64_t slot = ((int64_t)bh * n_rows + r) * 3 + st;
     const double inv = l[st] > 0.0 ? 1.0 / l[st] : 0.0;
-    part_acc[slot * D + lane] = (float)(acc0[st] * inv);
-    if (D == 128) part_acc[slot * D + lane + 64] = (float)(acc1[st] * inv);
+    float* acc = dst_acc[which[st]];
+    acc[lane] = (float)(acc0[st] * inv);
+    if (D == 128) acc[lane + 64] = (float)(acc1[st] * inv);
     if (lane == 0) {
-      part_ml[slot * 2 + 0] = (float)(m[st] * 1.4426950408889634);
-      part_ml[slot * 2 + 1] = l[st] > 0.0 ? 1.f : 0.f;
+      dst_ml[which[st]][0] = 0.f;
+      dst_ml[which[st]][1] = l[st] > 0.0 ? 1.f : 0.f;
     }
   }
 }
@@ -199,17 +205,17 @@ hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, i
 }
 
 hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                              const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml,
-                              hipStream_t st) {
+                              const int32_t* rows, int32_t n_rows, float* p1_acc, float* p1_ml, float* p2_acc,
+                              float* p2_ml, hipStream_t st) {
   dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
   const float *fq = static_cast<const float*>(q), *fk = static_cast<const float*>(k),
               *fv = static_cast<const float*>(v);
   if (g.d == 64)
-    hipLaunchKernelGGL(k_profile_f32<64>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, part_acc,
-                       part_ml);
+    hipLaunchKernelGGL(k_profile_f32<64>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, p1_acc, p1_ml,
+                       p2_acc, p2_ml);
   else
-    hipLaunchKernelGGL(k_profile_f32<128>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, part_acc,
-                       part_ml);
+    hipLaunchKernelGGL(k_profile_f32<128>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, p1_acc, p1_ml,
+                       p2_acc, p2_ml);
   return hipGetLastError();
 }
 

@@ -1,60 +1,122 @@
-// Merge of the profiling sweeps into per-head labels and statistics.
+// Profiling helpers: the position order of the sampled rows, and the merge of
+// the profiling sweeps into per-head labels and statistics.
 //
 // Profiling (rebuttal: answer on when profiling happens; abstract: online
 // prediction of each head's type) compares full attention with the spatial
 // and the temporal mask on the sampled rows:
 //   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
 //   label = SPATIAL if rel_s <= rel_t else TEMPORAL, FULL if min >= fallback.
-// One workgroup per head reduces the split partials (m in log2 units, l,
-// unnormalised acc) of every sampled row, in a fixed order, in fp64.
+// Sweep 1 leaves per row and key slice two partial states (m in log2 units,
+// l, unnormalised acc): IN (spatial keys) and OUT (the rest), or, with
+// full_direct, the spatial and the full output themselves; sweep 2 leaves the
+// temporal state.  Rows are merged in parallel, each row's three squared-error
+// sums are written, and one workgroup per head adds them in a fixed order.
 #include "svg_device.h"
 
 namespace svg {
 
-__global__ __launch_bounds__(256) void k_profile_merge(int32_t d, int32_t n_rows, int32_t ksplit,
-                                                       const float* __restrict__ part_acc,
-                                                       const float* __restrict__ part_ml, float fallback,
-                                                       int32_t* __restrict__ labels, float* __restrict__ stats) {
-  const int bh = blockIdx.x;
-  const int t = threadIdx.x;
-  double ss = 0.0, st = 0.0, sf = 0.0;
-  const int64_t n_el = (int64_t)n_rows * d;
-  for (int64_t e = t; e < n_el; e += 256) {
-    const int r = (int)(e / d), c = (int)(e % d);
-    float o[3];
-#pragma unroll
-    for (int s3 = 0; s3 < 3; ++s3) {
-      float mx = -INFINITY;
-      for (int k = 0; k < ksplit; ++k) {
-        const int64_t slot = (((int64_t)bh * n_rows + r) * ksplit + k) * 3 + s3;
-        mx = fmaxf(mx, part_ml[slot * 2]);
-      }
-      float l = 0.f, acc = 0.f;
-      if (mx != -INFINITY) {
-        for (int k = 0; k < ksplit; ++k) {
-          const int64_t slot = (((int64_t)bh * n_rows + r) * ksplit + k) * 3 + s3;
-          const float w = exp2f(part_ml[slot * 2] - mx);
-          l += w * part_ml[slot * 2 + 1];
-          acc += w * part_acc[slot * d + c];
-        }
-      }
-      o[s3] = l > 0.f ? acc / l : 0.f;
-    }
-    const double a = (double)o[1] - (double)o[0], b = (double)o[2] - (double)o[0];
-    ss += a * a;
-    st += b * b;
-    sf += (double)o[0] * (double)o[0];
+// Position order of the sampled rows (ascending, distinct video rows):
+// rank = #rows with a smaller position j, plus #rows at the same position in
+// earlier frames.  Each count is a binary search per frame.
+__device__ __forceinline__ int lower_bound_rows(const int32_t* rows, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rows[mid] < key)
+      lo = mid + 1;
+    else
+      hi = mid;
   }
+  return lo;
+}
+
+__global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n_rows, int32_t* __restrict__ ord_x,
+                            int32_t* __restrict__ ord_r) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const int x = rows[r];
+  const int u = x - g.T;
+  const int i = fastdiv(u, g.divF_mul, g.divF_shift), j = u - i * g.F;
+  int rank = 0;
+  for (int f = 0; f < g.N; ++f) {
+    const int fb = g.T + f * g.F;
+    const int a = lower_bound_rows(rows, n_rows, fb);
+    const int c = lower_bound_rows(rows, n_rows, fb + j);
+    rank += c - a;
+    if (f < i && c < n_rows && rows[c] == fb + j) ++rank;
+  }
+  ord_x[rank] = x;
+  ord_r[rank] = r;
+}
+
+// One workgroup (D threads, one per dim) per (sampled row, head).
+template <int D>
+__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit, int32_t full_direct,
+                                                       const float* __restrict__ p1_acc,
+                                                       const float* __restrict__ p1_ml,
+                                                       const float* __restrict__ p2_acc,
+                                                       const float* __restrict__ p2_ml, double* __restrict__ row_sums) {
+  const int r = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+  const int64_t row = (int64_t)bh * n_rows + r;
+  // states 0 and 1 of sweep 1, merged over the key slices
+  float m[2] = {-INFINITY, -INFINITY};
+  for (int s = 0; s < ksplit; ++s)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) m[st] = fmaxf(m[st], p1_ml[((row * ksplit + s) * 2 + st) * 2]);
+  float l[2] = {0.f, 0.f}, a[2] = {0.f, 0.f};
+  for (int s = 0; s < ksplit; ++s)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (m[st] == -INFINITY) continue;
+      const int64_t slot = (row * ksplit + s) * 2 + st;
+      const float w = exp2f(p1_ml[slot * 2] - m[st]);
+      l[st] += w * p1_ml[slot * 2 + 1];
+      a[st] += w * p1_acc[slot * D + c];
+    }
+  const float o_sp = l[0] > 0.f ? a[0] / l[0] : 0.f;
+  float o_f;
+  if (full_direct) {
+    o_f = l[1] > 0.f ? a[1] / l[1] : 0.f;
+  } else {  // full = IN combined with OUT
+    const float mm = fmaxf(m[0], m[1]);
+    const float w0 = m[0] == -INFINITY ? 0.f : exp2f(m[0] - mm), w1 = m[1] == -INFINITY ? 0.f : exp2f(m[1] - mm);
+    const float lf = l[0] * w0 + l[1] * w1;
+    o_f = lf > 0.f ? (a[0] * w0 + a[1] * w1) / lf : 0.f;
+  }
+  const float lt = p2_ml[row * 2 + 1];
+  const float o_tp = lt > 0.f ? p2_acc[row * D + c] / lt : 0.f;
+  const double ds = (double)o_sp - (double)o_f, dt = (double)o_tp - (double)o_f;
+  __shared__ double red[3][D];
+  red[0][c] = ds * ds;
+  red[1][c] = dt * dt;
+  red[2][c] = (double)o_f * (double)o_f;
+  __syncthreads();
+  for (int w = D / 2; w > 0; w >>= 1) {
+    if (c < w) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) red[k][c] += red[k][c + w];
+    }
+    __syncthreads();
+  }
+  if (c < 3) row_sums[row * 3 + c] = red[c][0];
+}
+
+__global__ __launch_bounds__(256) void k_prof_finalize(int32_t d, int32_t n_rows, const double* __restrict__ row_sums,
+                                                       float fallback, int32_t* __restrict__ labels,
+                                                       float* __restrict__ stats) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  double acc[3] = {0.0, 0.0, 0.0};
+  for (int r = t; r < n_rows; r += 256)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) acc[k] += row_sums[((int64_t)bh * n_rows + r) * 3 + k];
   __shared__ double red[3][256];
-  red[0][t] = ss;
-  red[1][t] = st;
-  red[2][t] = sf;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) red[k][t] = acc[k];
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (t < w) {
-      red[0][t] += red[0][t + w];
-      red[1][t] += red[1][t + w];
-      red[2][t] += red[2][t + w];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) red[k][t] += red[k][t + w];
     }
     __syncthreads();
   }
@@ -66,15 +128,29 @@ __global__ __launch_bounds__(256) void k_profile_merge(int32_t d, int32_t n_rows
     labels[bh] = best >= (double)fallback ? SVG_FULL : (rs <= rt ? SVG_SPATIAL : SVG_TEMPORAL);
     stats[bh * 3 + 0] = (float)rs;
     stats[bh * 3 + 1] = (float)rt;
-    stats[bh * 3 + 2] = (float)(den / (double)n_el);
+    stats[bh * 3 + 2] = (float)(den / ((double)n_rows * d));
   }
 }
 
-hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
-                                const float* part_ml, float fallback, int32_t* labels, float* stats,
-                                hipStream_t st) {
-  hipLaunchKernelGGL(k_profile_merge, dim3((unsigned)(g.B * g.H)), dim3(256), 0, st, g.d, n_rows, ksplit,
-                     part_acc, part_ml, fallback, labels, stats);
+hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_prof_rank, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, st, g, rows, n_rows, ord_x,
+                     ord_r);
+  return hipGetLastError();
+}
+
+hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t full_direct,
+                                const float* p1_acc, const float* p1_ml, const float* p2_acc, const float* p2_ml,
+                                double* row_sums, float fallback, int32_t* labels, float* stats, hipStream_t st) {
+  dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
+  if (g.d == 64)
+    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, full_direct, p1_acc, p1_ml,
+                       p2_acc, p2_ml, row_sums);
+  else
+    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, full_direct, p1_acc, p1_ml,
+                       p2_acc, p2_ml, row_sums);
+  hipLaunchKernelGGL(k_prof_finalize, dim3((unsigned)(g.B * g.H)), dim3(256), 0, st, g.d, n_rows, row_sums, fallback,
+                     labels, stats);
   return hipGetLastError();
 }
 

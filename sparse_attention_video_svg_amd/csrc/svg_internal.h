@@ -39,7 +39,8 @@ __device__ __forceinline__ int32_t fastdiv(int32_t n, uint32_t mul, uint32_t shi
 
 // Workspace carve-up for svg_layer_forward / svg_profile_heads.
 struct WsLayout {
-  size_t labels, ranges, order, part_acc, part_ml, perm, total;
+  size_t p1_acc, p1_ml, p2_acc, p2_ml, row_sums, ord_x, ord_r;  // profiling
+  size_t labels, ranges, order, perm, total;
   size_t perm_tensor_bytes;  // one permuted tensor (all heads)
   int32_t ksplit;            // key splits of the profiling sweep
 };
@@ -60,17 +61,22 @@ struct AttnPtrs {
 hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, int32_t BN, hipStream_t st);
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st);
 
-// Profiling: partial sweeps write (m, l, acc) per (head, row, split, state);
-// the merge kernel reduces them, deterministically, into labels and stats.
+// Profiling: sweep 1 (frame-major keys) writes per (head, row, key slice)
+// two partial states (m, l, acc); sweep 2 (token-major keys, rows in position
+// order) writes the temporal state; the merge reduces them, deterministically,
+// into labels and stats.
+hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
+                               hipStream_t st);
 hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                              const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml,
-                              hipStream_t st);
+                              const int32_t* rows, int32_t n_rows, float* p1_acc, float* p1_ml, float* p2_acc,
+                              float* p2_ml, hipStream_t st);
 hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                               const int32_t* rows, int32_t n_rows, int32_t ksplit, float* part_acc,
-                               float* part_ml, hipStream_t st);
-hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
-                                const float* part_ml, float fallback, int32_t* labels, float* stats,
-                                hipStream_t st);
+                               const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                               const int32_t* ord_r, float* p1_acc, float* p1_ml, float* p2_acc, float* p2_ml,
+                               hipStream_t st);
+hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t full_direct,
+                                const float* p1_acc, const float* p1_ml, const float* p2_acc, const float* p2_ml,
+                                double* row_sums, float fallback, int32_t* labels, float* stats, hipStream_t st);
 
 // Tile sizes of the bf16 MFMA attention kernel and of the fp32 kernel.
 constexpr int32_t kBM_bf16 = 128, kBN_bf16 = 64;
