@@ -78,6 +78,7 @@ svg_status check_ptr(const void* p, const char* name, size_t align) {
 
 svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const char* name) {
   if (s.x < g.d) return fail(SVG_E_INVALID, "%s: token stride %lld < d", name, (long long)s.x);
+  if (s.x > (1 << 24)) return fail(SVG_E_UNSUPPORTED, "%s: token stride %lld > 2^24", name, (long long)s.x);
   if (s.h < 0 || s.b < 0) return fail(SVG_E_INVALID, "%s: negative stride", name);
   if ((s.x * elt) % 16 || (s.h * elt) % 16 || (s.b * elt) % 16)
     return fail(SVG_E_INVALID, "%s: strides must be multiples of 16 bytes", name);

@@ -55,28 +55,64 @@ struct TileCfg {
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the direct-to-LDS loads of one K tile and one V tile (all 256 threads).
-// Chunk p of the tile (row r = p / CR, LDS position pos = p % CR) receives
-// global chunk pos ^ swz(r) of key row kt0 + r (clamped to the last row).
-template <int D, typename RowMap>
-__device__ __forceinline__ void load_kv_tile(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                                             int64_t sx, int kt0, int L, RowMap phys, __bf16* lds_k,
-                                             __bf16* lds_v, int wave, int lane) {
+// Direct-to-LDS loads of one K tile and one V tile by all 256 threads.
+// Chunk p of a tile (row r = p / CR, LDS position pos = p % CR) receives
+// global chunk pos ^ swz(r) of key row kt0 + r.  Each lane's byte offsets
+// within a tile are fixed, so the hot path is one scalar base per tile plus
+// the lane's 32-bit offset (the saddr form of the load).  The last, ragged
+// tile clamps rows to L - 1; with VIRT the rows are gathered through the
+// token-major index map.
+template <int D, bool VIRT>
+struct KVLoader {
   using C = TileCfg<D>;
+  const char* kb;
+  const char* vb;
+  int64_t sxb;  // token stride in bytes
+  uint32_t offk[C::LOADS], offv[C::LOADS];
+  int L;
+
+  __device__ __forceinline__ void init(const __bf16* K, const __bf16* V, int64_t sx, int L_, int wave, int lane) {
+    kb = reinterpret_cast<const char*>(K);
+    vb = reinterpret_cast<const char*>(V);
+    sxb = sx * 2;
+    L = L_;
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int seg = i * 4 + wave;  // 64-chunk segment written by this instruction
-    const int p = seg * 64 + lane;
-    const int r = p / C::CR, pos = p % C::CR;
-    int row = kt0 + r;
-    row = row < L ? row : L - 1;
-    const int64_t off = (int64_t)phys(row) * sx;
-    const __bf16* gk = K + off + ((pos ^ C::swz_k(r)) * 8);
-    const __bf16* gv = V + off + ((pos ^ C::swz_v(r)) * 8);
-    __builtin_amdgcn_global_load_lds((const void*)gk, (SVG_LDS void*)(lds_k + seg * 64 * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)gv, (SVG_LDS void*)(lds_v + seg * 64 * 8), 16, 0, 0);
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int p = (i * 4 + wave) * 64 + lane;
+      const int r = p / C::CR, pos = p % C::CR;
+      offk[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_k(r)) * 16);
+      offv[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_v(r)) * 16);
+    }
   }
-}
+
+  __device__ __forceinline__ void load(const KGeom& g, int kt0, __bf16* lds_k, __bf16* lds_v, int wave, int lane) const {
+    if (!VIRT && kt0 + kBN <= L) {
+      const char* kt = kb + kt0 * sxb;
+      const char* vt = vb + kt0 * sxb;
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int seg = i * 4 + wave;
+        __builtin_amdgcn_global_load_lds((const void*)(kt + offk[i]), (SVG_LDS void*)(lds_k + seg * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + offv[i]), (SVG_LDS void*)(lds_v + seg * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int seg = i * 4 + wave;
+        const int p = seg * 64 + lane;
+        const int r = p / C::CR, pos = p % C::CR;
+        int row = kt0 + r;
+        row = row < L ? row : L - 1;
+        if (VIRT) row = perm_inv_row(g, row);
+        const int64_t off = (int64_t)row * sxb;
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off + (pos ^ C::swz_k(r)) * 16),
+                                         (SVG_LDS void*)(lds_k + seg * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + off + (pos ^ C::swz_v(r)) * 16),
+                                         (SVG_LDS void*)(lds_v + seg * 512), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // S^T block (32 keys x 32 queries) for key block kb2 of the tile in LDS.
 template <int D>
@@ -181,11 +217,14 @@ struct Flash {
 
 // Mask the raw scores of a tile to the lane's active keys [0, T) U [lo, hi).
 __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt0, int hh, int T, int lo, int hi) {
+  const unsigned span = (unsigned)(hi - lo);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int k0 = kt0 + acc_key(0, r, hh), k1 = kt0 + acc_key(1, r, hh);
-    if (!(k0 < T || (k0 >= lo && k0 < hi))) s0[r] = -INFINITY;
-    if (!(k1 < T || (k1 >= lo && k1 < hi))) s1[r] = -INFINITY;
+    const bool a0 = (k0 < T) | ((unsigned)(k0 - lo) < span);
+    const bool a1 = (k1 < T) | ((unsigned)(k1 - lo) < span);
+    s0[r] = a0 ? s0[r] : -INFINITY;
+    s1[r] = a1 ? s1[r] : -INFINITY;
   }
 }
 
@@ -193,11 +232,13 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt0, int h
 // ranges [rg.x, rg.y) U [rg.z, rg.w) of key tiles.  Every lane's active keys
 // are [0, T) U [lo, hi); `valid` marks lanes with a real query row.  The
 // caller has already issued the loads of the first tile into buffer 0.
-template <int D, typename RowMap>
-__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const __bf16* K, const __bf16* V, int64_t sx,
-                                      RowMap phys, int4 rg, int L, int T, int lo, int hi, bool valid, float sl2,
-                                      __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+template <int D, bool VIRT>
+__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLoader<D, VIRT>& ld, const KGeom& g,
+                                      int4 rg, int lo, int hi, bool valid, __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS],
+                                      int wave, int lane) {
   const int hh = lane >> 5;
+  const int T = g.T;
+  const float sl2 = g.scale_log2;
   const int n1 = rg.y - rg.x, nt = n1 + (rg.w - rg.z);
   auto tile_of = [&](int t) { return t < n1 ? rg.x + t : rg.z + (t - n1); };
   // wave-wide run bounds over valid rows: a tile is full for the wave when it
@@ -212,7 +253,7 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const __bf
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     const int bf = t & 1;
-    if (t + 1 < nt) load_kv_tile<D>(K, V, sx, tile_of(t + 1) * kBN, L, phys, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
+    if (t + 1 < nt) ld.load(g, tile_of(t + 1) * kBN, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
     const int kt0 = tile_of(t) * kBN, kt1 = kt0 + kBN;
     const bool idle = kt0 >= T && (kt1 <= min_lo || kt0 >= max_hi);
     if (wave_rows && !idle) {
@@ -228,6 +269,8 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const __bf
   }
 }
 
+__device__ __forceinline__ int nqt_of(const KGeom& g) { return (g.L + kBM - 1) / kBM; }
+
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int hh) {
   const __bf16* qrow = qrow_base + 8 * hh;
@@ -235,24 +278,14 @@ __device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int 
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
 }
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT, int32_t total) {
-  using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];  // [buffer][K, V]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5;
-
-  // XCD-aware remap of the workgroup id, then longest-head-first order.
-  const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
-  if (logical >= total) return;
-  const int bh = a.order[logical / nQT];
-  const int qt = logical % nQT;
+// One query tile of one head.  VIRT: a temporal head read and written through
+// the token-major index map instead of explicitly permuted copies.
+template <int D, bool OUT_BF16, bool VIRT>
+__device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int bh, int qt, int mode,
+                                          __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+  const int hh = lane >> 5;
   const int b = bh / g.H, h = bh % g.H;
-  const int mode = a.modes[bh];
-  const bool temporal = mode == SVG_TEMPORAL;
-  const bool virt = temporal && (a.flags & SVG_FLAG_VIRTUAL_PERMUTE);
-  const bool use_p = temporal && !virt;
+  const bool use_p = mode == SVG_TEMPORAL && !VIRT;
   const svg_strides sin = use_p ? a.sp : a.s;
   const svg_strides sout = use_p ? a.sop : a.so;
   const int64_t ibase = (int64_t)b * sin.b + (int64_t)h * sin.h;
@@ -262,26 +295,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
   const __bf16* V = static_cast<const __bf16*>(use_p ? a.vp : a.v) + ibase;
   char* O = static_cast<char*>(use_p ? a.op : a.o);
   constexpr int OE = OUT_BF16 ? 2 : 4;  // output element bytes
-  const int row0 = qt * kBM;
-  const KGeom gg = g;
-  auto phys = [gg, virt](int r) { return virt ? perm_inv_row(gg, r) : r; };
+  auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
 
-  if (mode == SVG_SKIP) {  // Sparse-vDiT head skipping: the output is zero
-    constexpr int CPRO = D * OE / 16;
-    for (int c = tid; c < kBM * CPRO; c += 256) {
-      const int r = row0 + c / CPRO;
-      if (r < g.L)
-        *reinterpret_cast<int4*>(O + (obase + (int64_t)r * sout.x) * OE + (c % CPRO) * 16) = make_int4(0, 0, 0, 0);
-    }
-    return;
-  }
-
-  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
-  if (rg.y > rg.x) load_kv_tile<D>(K, V, sin.x, rg.x * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
-  else if (rg.w > rg.z) load_kv_tile<D>(K, V, sin.x, rg.z * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
+  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nqt_of(g) + qt];
+  KVLoader<D, VIRT> ld;
+  ld.init(K, V, sin.x, g.L, wave, lane);
+  if (rg.y > rg.x)
+    ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
+  else if (rg.w > rg.z)
+    ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
 
   // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
-  const int xq = row0 + wave * 32 + (lane & 31);
+  const int xq = qt * kBM + wave * 32 + (lane & 31);
   const bool valid = xq < g.L;
   const int xqc = valid ? xq : g.L - 1;
   bf16x8 qf[D / 16];
@@ -290,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
   row_interval(g, mode, xqc, lo, hi);
 
   Flash<D> st;
-  sweep<D>(st, qf, K, V, sin.x, phys, rg, g.L, g.T, lo, hi, valid, g.scale_log2, lds, wave, lane);
+  sweep<D, VIRT>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
 
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
   const float l_tot = half_sum(st.l_part);
@@ -313,6 +338,41 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
       }
     }
   }
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT, int32_t total) {
+  using C = TileCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];  // [buffer][K, V]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // XCD-aware remap of the workgroup id, then longest-head-first order.
+  const int w = blockIdx.x;
+  const int xcd = w & 7, slot = w >> 3;
+  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  if (logical >= total) return;
+  const int bh = a.order[logical / nQT];
+  const int qt = logical % nQT;
+  const int mode = a.modes[bh];
+
+  if (mode == SVG_SKIP) {  // Sparse-vDiT head skipping: the output is zero
+    constexpr int OE = OUT_BF16 ? 2 : 4;
+    constexpr int CPRO = D * OE / 16;
+    const int b = bh / g.H, h = bh % g.H;
+    const int64_t obase = (int64_t)b * a.so.b + (int64_t)h * a.so.h;
+    char* O = static_cast<char*>(a.o);
+    for (int c = tid; c < kBM * CPRO; c += 256) {
+      const int r = qt * kBM + c / CPRO;
+      if (r < g.L)
+        *reinterpret_cast<int4*>(O + (obase + (int64_t)r * a.so.x) * OE + (c % CPRO) * 16) = make_int4(0, 0, 0, 0);
+    }
+    return;
+  }
+  if (mode == SVG_TEMPORAL && (a.flags & SVG_FLAG_VIRTUAL_PERMUTE))
+    attn_tile<D, OUT_BF16, true>(g, a, bh, qt, mode, lds, wave, lane);
+  else
+    attn_tile<D, OUT_BF16, false>(g, a, bh, qt, mode, lds, wave, lane);
 }
 
 // Partial (m, l, acc) of one output of one sampled row: acc in the
@@ -351,18 +411,18 @@ __global__ __launch_bounds__(256, 1) void k_prof_spatial(KGeom g, const __bf16* 
                                                          float* __restrict__ part_ml) {
   using C = TileCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x, split = blockIdx.y, bh = blockIdx.z;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  const __bf16* K = k + base;
-  const __bf16* V = v + base;
-  auto ident = [](int r) { return r; };
+  KVLoader<D, false> ld;
+  ld.init(k + base, v + base, s.x, g.L, wave, lane);
 
   const int nKT = (g.L + kBN - 1) / kBN;
   const int t_begin = (int)((int64_t)nKT * split / ksplit), t_end = (int)((int64_t)nKT * (split + 1) / ksplit);
   const int nt = t_end - t_begin;
-  if (nt > 0) load_kv_tile<D>(K, V, s.x, t_begin * kBN, g.L, ident, lds[0][0], lds[0][1], wave, lane);
+  if (nt > 0) ld.load(g, t_begin * kBN, lds[0][0], lds[0][1], wave, lane);
 
   const int ridx = chunk * kProfRows_bf16 + wave * 32 + (lane & 31);
   const bool valid = ridx < n_rows;
@@ -385,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void k_prof_spatial(KGeom g, const __bf16* 
   for (int t = 0; t < nt; ++t) {
     const int bf = t & 1;
     if (t + 1 < nt)
-      load_kv_tile<D>(K, V, s.x, (t_begin + t + 1) * kBN, g.L, ident, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
+      ld.load(g, (t_begin + t + 1) * kBN, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
     const int kt0 = (t_begin + t) * kBN, kt1 = kt0 + kBN;
     const __bf16* lk = lds[bf][0];
     const __bf16* lv = lds[bf][1];
@@ -438,14 +498,13 @@ __global__ __launch_bounds__(256, 2) void k_prof_temporal(KGeom g, const __bf16*
   using C = TileCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];
   __shared__ int wb[2][4];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  const __bf16* K = k + base;
-  const __bf16* V = v + base;
-  const KGeom gg = g;
-  auto phys = [gg](int r) { return perm_inv_row(gg, r); };
+  KVLoader<D, true> ld;
+  ld.init(k + base, v + base, s.x, g.L, wave, lane);
 
   const int rk = chunk * kProfRows_bf16 + wave * 32 + (lane & 31);
   const bool valid = rk < n_rows;
@@ -470,12 +529,12 @@ __global__ __launch_bounds__(256, 2) void k_prof_temporal(KGeom g, const __bf16*
     rg = make_int4(0, max(be, te), 0, 0);
   else
     rg = make_int4(0, te, bs, be);
-  load_kv_tile<D>(K, V, s.x, rg.x * kBN, g.L, phys, lds[0][0], lds[0][1], wave, lane);
+  ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
 
   bf16x8 qf[D / 16];
   load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
   Flash<D> st;
-  sweep<D>(st, qf, K, V, s.x, phys, rg, g.L, g.T, lo, hi, valid, g.scale_log2, lds, wave, lane);
+  sweep<D, true>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
     const int64_t slot = (int64_t)bh * n_rows + ord_r[rk];
     store_partial<D>(st, part_acc + slot * D, part_ml + slot * 2, hh);
