@@ -31,6 +31,8 @@
 //    the 8 XCDs) walks runs of consecutive query tiles of one head, which
 //    share their K/V band in that XCD's L2; runs are handed out in the
 //    longest-head-first order of svg_build_blocks.
+#include <type_traits>
+
 #include "svg_device.h"
 
 namespace svg {
@@ -85,15 +87,17 @@ struct KVLoader {
     }
   }
 
-  __device__ __forceinline__ void load(const KGeom& g, int kt0, __bf16* lds_k, __bf16* lds_v, int wave, int lane) const {
+  // one tensor (K: which = 0, V: which = 1) of the tile at key kt0
+  template <int WHICH>
+  __device__ __forceinline__ void load1(const KGeom& g, int kt0, __bf16* lds_t, int wave, int lane) const {
+    const char* base = WHICH == 0 ? kb : vb;
     if (!VIRT && kt0 + kBN <= L) {
-      const char* kt = kb + kt0 * sxb;
-      const char* vt = vb + kt0 * sxb;
+      const char* tb = base + kt0 * sxb;
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const int seg = i * 4 + wave;
-        __builtin_amdgcn_global_load_lds((const void*)(kt + offk[i]), (SVG_LDS void*)(lds_k + seg * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + offv[i]), (SVG_LDS void*)(lds_v + seg * 512), 16, 0, 0);
+        const uint32_t off = WHICH == 0 ? offk[i] : offv[i];
+        __builtin_amdgcn_global_load_lds((const void*)(tb + off), (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
@@ -104,13 +108,16 @@ struct KVLoader {
         int row = kt0 + r;
         row = row < L ? row : L - 1;
         if (VIRT) row = perm_inv_row(g, row);
-        const int64_t off = (int64_t)row * sxb;
-        __builtin_amdgcn_global_load_lds((const void*)(kb + off + (pos ^ C::swz_k(r)) * 16),
-                                         (SVG_LDS void*)(lds_k + seg * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + off + (pos ^ C::swz_v(r)) * 16),
-                                         (SVG_LDS void*)(lds_v + seg * 512), 16, 0, 0);
+        const int sw = WHICH == 0 ? C::swz_k(r) : C::swz_v(r);
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)row * sxb + (pos ^ sw) * 16),
+                                         (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
       }
     }
+  }
+
+  __device__ __forceinline__ void load(const KGeom& g, int kt0, __bf16* lds_k, __bf16* lds_v, int wave, int lane) const {
+    load1<0>(g, kt0, lds_k, wave, lane);
+    load1<1>(g, kt0, lds_v, wave, lane);
   }
 };
 
@@ -203,9 +210,16 @@ struct Flash {
       for (int r = 0; r < 8; ++r) {
         const float sv = (s16 >> 1) ? s1[(s16 & 1) * 8 + r] : s0[(s16 & 1) * 8 + r];
         p8[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sl2, nmu));
-        l_part += p8[r];
       }
       const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+      // row sum of the bf16 weights the P.V product actually uses, two per
+      // v_dot2_f32_bf16 against (1, 1)
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part, false);
+      }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
@@ -251,21 +265,26 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLo
   st.init();
   wait_vm_all();
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int bf = t & 1;
+  // one tile: prefetch the next into the other buffer, compute, sync
+  auto step = [&](int t, auto bfc) {
+    constexpr int bf = decltype(bfc)::value;
     if (t + 1 < nt) ld.load(g, tile_of(t + 1) * kBN, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
     const int kt0 = tile_of(t) * kBN, kt1 = kt0 + kBN;
     const bool idle = kt0 >= T && (kt1 <= min_lo || kt0 >= max_hi);
     if (wave_rows && !idle) {
       const bool full = (kt1 <= T) || (max(kt0, T) >= max_lo && kt1 <= min_hi);
-      const __bf16* lk = lds[bf][0];
-      f32x16 s0 = score_block<D>(lk, qf, 0, lane);
-      f32x16 s1 = score_block<D>(lk, qf, 1, lane);
+      f32x16 s0 = score_block<D>(lds[bf][0], qf, 0, lane);
+      f32x16 s1 = score_block<D>(lds[bf][0], qf, 1, lane);
       if (!full) mask_tile(s0, s1, kt0, hh, T, lo, hi);
       st.add_tile(s0, s1, lds[bf][1], lane, sl2);
     }
     wait_vm_all();
     __syncthreads();
+  };
+  // unrolled by two so that each buffer's LDS offsets are immediates
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
   }
 }
 
