@@ -60,6 +60,30 @@ def pair_count(N, F, T, mode, a1=1, a2=1, window=1, stripe=1):
     return text + vid
 
 
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_attn_bf16_hunyuanvideo_33x3600_h24_d128.md")
+ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_video_svg_amd", "csrc", "attn_bf16.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per attention dispatch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(PROFILE_SUMMARY).read()
+        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    rec = {}
+    for line in text.splitlines():
+        if line.startswith("- attn_"):
+            k, _, v = line[2:].partition(":")
+            rec[k.strip()] = v.strip()
+    if rec.get("attn_kernel_source_sha256") != sha or "attn_traffic_bytes_per_dispatch" not in rec:
+        return None
+    return float(rec["attn_traffic_bytes_per_dispatch"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -86,17 +110,18 @@ def cpu_baseline(cfg, inp, labels, d, scale, budget_s=12.0):
     elapsed = 0.0
     rows_done = 0
     n = 8
-    while elapsed < budget_s and n <= L:
+    while elapsed < budget_s:
+        m = min(n, L)
         for h in heads:
-            rows = np.sort(rng.choice(L, size=n, replace=False)).astype(np.int64)
+            rows = np.sort(rng.choice(L, size=m, replace=False)).astype(np.int64)
             t0 = time.perf_counter()
             oracle.attention_rows(og, int(labels[h]), inp["q"][h], inp["k"][h], inp["v"][h], scale, rows)
             elapsed += time.perf_counter() - t0
             for r in rows:
                 iv = oracle.row_intervals(og, oracle.TEMPORAL if labels[h] == 1 else int(labels[h]), int(r))
                 flops += 4.0 * d * sum(hi - lo for lo, hi in iv)
-            rows_done += n
-        n *= 2
+            rows_done += m
+        n = min(2 * n, 2048)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{rows_done} seeded query rows of heads {heads} (labels "
                       f"{[int(labels[h]) for h in heads]}), fp64 oracle masked attention, {elapsed:.1f} s"}
@@ -249,7 +274,8 @@ def main():
         "permute_inv_gbs": None if inv_gbs is None else round(inv_gbs, 1),
         "effective_flops_per_layer": flops,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "frac": round(attn_tflops / peak, 4),
+                     "traffic": recorded_traffic() if args.config == 2 and not args.virtual else None,
                      "kernel": "k_attn_bf16 (svg_sparse_attention)" if bf16 else "k_attn_f32"},
     }
     if not args.no_cpu:
