@@ -37,16 +37,16 @@
 
 namespace svg {
 
-constexpr int kBM = kBM_bf16, kBN = kBN_bf16;
+constexpr int kBN = kBN_bf16;
 constexpr float kRescaleTau = 8.0f;  // log2 headroom before the running max moves
 constexpr int kXcdRun = 32;          // consecutive query tiles per XCD turn
 
-template <int D>
+template <int D, int WAVES = 4>
 struct TileCfg {
   static constexpr int CR = D / 8;                   // 16-byte chunks per row
   static constexpr int RPL = 16 / CR;                // rows per 256-byte LDS line
   static constexpr int CHUNKS = kBN * CR;            // chunks per K (or V) tile
-  static constexpr int LOADS = CHUNKS / 256;         // per thread per tensor
+  static constexpr int LOADS = CHUNKS / (64 * WAVES);  // per thread per tensor
   static constexpr int TILE_ELEMS = kBN * D;         // bf16 elements per tile
   // K rows are read 16 keys x one chunk at a time: spread keys over chunks.
   __device__ static __forceinline__ int swz_k(int r) { return (r / RPL) % CR; }
@@ -56,6 +56,12 @@ struct TileCfg {
 };
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Direct-to-LDS loads of one K tile and one V tile by all 256 threads.
 // Chunk p of a tile (row r = p / CR, LDS position pos = p % CR) receives
@@ -64,9 +70,9 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // the lane's 32-bit offset (the saddr form of the load).  The last, ragged
 // tile clamps rows to L - 1; with VIRT the rows are gathered through the
 // token-major index map.
-template <int D, bool VIRT>
+template <int D, bool VIRT, int WAVES = 4>
 struct KVLoader {
-  using C = TileCfg<D>;
+  using C = TileCfg<D, WAVES>;
   const char* kb;
   const char* vb;
   int64_t sxb;  // token stride in bytes
@@ -80,7 +86,7 @@ struct KVLoader {
     L = L_;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane;
+      const int p = (i * WAVES + wave) * 64 + lane;
       const int r = p / C::CR, pos = p % C::CR;
       offk[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_k(r)) * 16);
       offv[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_v(r)) * 16);
@@ -95,14 +101,14 @@ struct KVLoader {
       const char* tb = base + kt0 * sxb;
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
-        const int seg = i * 4 + wave;
+        const int seg = i * WAVES + wave;
         const uint32_t off = WHICH == 0 ? offk[i] : offv[i];
         __builtin_amdgcn_global_load_lds((const void*)(tb + off), (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
-        const int seg = i * 4 + wave;
+        const int seg = i * WAVES + wave;
         const int p = seg * 64 + lane;
         const int r = p / C::CR, pos = p % C::CR;
         int row = kt0 + r;
@@ -136,6 +142,44 @@ __device__ __forceinline__ f32x16 score_block(const __bf16* lds_k, const bf16x8*
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc, 0, 0, 0);
   }
   return acc;
+}
+
+// Both 32-key blocks of a tile, the two accumulation chains interleaved and
+// the K fragments read kAhead steps before their MFMAs, so LDS latency hides
+// behind matrix work instead of stalling every pair of MFMAs.
+template <int D>
+__device__ __forceinline__ void score_tile(const __bf16* lds_k, const bf16x8* qf, int lane, f32x16& s0, f32x16& s1) {
+  using C = TileCfg<D>;
+  constexpr int KS = D / 16, kAhead = 3;
+  const int hh = lane >> 5;
+  const int m0 = lane & 31, m1 = 32 + (lane & 31);
+  const int sw0 = C::swz_k(m0), sw1 = C::swz_k(m1);
+  auto rd = [&](int m, int sw, int ks) {
+    return *reinterpret_cast<const bf16x8*>(lds_k + m * D + (((2 * ks + hh) ^ sw) * 8));
+  };
+  bf16x8 f0[KS], f1[KS];
+#pragma unroll
+  for (int ks = 0; ks < kAhead; ++ks) {
+    f0[ks] = rd(m0, sw0, ks);
+    f1[ks] = rd(m1, sw1, ks);
+  }
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + kAhead < KS) {
+      f0[ks + kAhead] = rd(m0, sw0, ks + kAhead);
+      f1[ks + kAhead] = rd(m1, sw1, ks + kAhead);
+    }
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[ks], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[ks], qf[ks], s1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {  // keep the issue order: 2 reads, then 2 MFMAs
+    if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+    if (i + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
 }
 
 // V^T fragment (32 dims x 16 keys) of key step s16 and dim block db, in the
@@ -245,11 +289,14 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt0, int h
 // Single-output flash sweep of a workgroup over a tile sequence given as two
 // ranges [rg.x, rg.y) U [rg.z, rg.w) of key tiles.  Every lane's active keys
 // are [0, T) U [lo, hi); `valid` marks lanes with a real query row.  The
-// caller has already issued the loads of the first tile into buffer 0.
-template <int D, bool VIRT>
-__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLoader<D, VIRT>& ld, const KGeom& g,
-                                      int4 rg, int lo, int hi, bool valid, __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS],
-                                      int wave, int lane) {
+// caller has already issued the loads of the first tile into stage 0.  K/V
+// tiles go through a ring of STAGES LDS buffers: tile t + STAGES - 1 is in
+// flight while tile t is computed, with one barrier per tile.
+template <int D, bool VIRT, int WAVES, int STAGES>
+__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLoader<D, VIRT, WAVES>& ld,
+                                      const KGeom& g, int4 rg, int lo, int hi, bool valid,
+                                      __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+  constexpr int PER_TILE = 2 * TileCfg<D, WAVES>::LOADS;  // load instructions per tile per wave
   const int hh = lane >> 5;
   const int T = g.T;
   const float sl2 = g.scale_log2;
@@ -263,32 +310,42 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLo
   const int max_hi = wave_max_i(valid ? hi : INT_MIN);
   const bool wave_rows = wave_max_i(valid ? 1 : 0) != 0;
   st.init();
-  wait_vm_all();
+  // prologue: tiles 1 .. STAGES-2 into their stages, then wait for tile 0
+#pragma unroll
+  for (int p = 1; p <= STAGES - 2; ++p)
+    if (p < nt) ld.load(g, tile_of(p) * kBN, lds[p][0], lds[p][1], wave, lane);
+  if (STAGES == 3 && nt > 1)
+    wait_vm<PER_TILE>();
+  else
+    wait_vm_all();
   __syncthreads();
-  // one tile: prefetch the next into the other buffer, compute, sync
-  auto step = [&](int t, auto bfc) {
-    constexpr int bf = decltype(bfc)::value;
-    if (t + 1 < nt) ld.load(g, tile_of(t + 1) * kBN, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
+  auto step = [&](int t, auto stc) {
+    constexpr int sg = decltype(stc)::value;  // t % STAGES
+    constexpr int nx = (sg + STAGES - 1) % STAGES;
+    if (t + STAGES - 1 < nt) ld.load(g, tile_of(t + STAGES - 1) * kBN, lds[nx][0], lds[nx][1], wave, lane);
     const int kt0 = tile_of(t) * kBN, kt1 = kt0 + kBN;
     const bool idle = kt0 >= T && (kt1 <= min_lo || kt0 >= max_hi);
     if (wave_rows && !idle) {
       const bool full = (kt1 <= T) || (max(kt0, T) >= max_lo && kt1 <= min_hi);
-      f32x16 s0 = score_block<D>(lds[bf][0], qf, 0, lane);
-      f32x16 s1 = score_block<D>(lds[bf][0], qf, 1, lane);
+      f32x16 s0, s1;
+      score_tile<D>(lds[sg][0], qf, lane, s0, s1);
       if (!full) mask_tile(s0, s1, kt0, hh, T, lo, hi);
-      st.add_tile(s0, s1, lds[bf][1], lane, sl2);
+      st.add_tile(s0, s1, lds[sg][1], lane, sl2);
     }
-    wait_vm_all();
+    // tile t+1 must have landed; later tiles may still be in flight
+    if (STAGES == 3 && t + 2 < nt)
+      wait_vm<PER_TILE>();
+    else
+      wait_vm_all();
     __syncthreads();
   };
-  // unrolled by two so that each buffer's LDS offsets are immediates
-  for (int t = 0; t < nt; t += 2) {
+  // unrolled by STAGES so that each buffer's LDS offsets are immediates
+  for (int t = 0; t < nt; t += STAGES) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1 % STAGES>{});
+    if (STAGES == 3 && t + 2 < nt) step(t + 2, std::integral_constant<int, 2 % STAGES>{});
   }
 }
-
-__device__ __forceinline__ int nqt_of(const KGeom& g) { return (g.L + kBM - 1) / kBM; }
 
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int hh) {
@@ -297,11 +354,13 @@ __device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int 
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
 }
 
-// One query tile of one head.  VIRT: a temporal head read and written through
-// the token-major index map instead of explicitly permuted copies.
-template <int D, bool OUT_BF16, bool VIRT>
-__device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int bh, int qt, int mode,
+// One query tile (32 * WAVES rows) of one head.  VIRT: a temporal head read
+// and written through the token-major index map instead of explicitly
+// permuted copies.
+template <int D, bool OUT_BF16, bool VIRT, int WAVES, int STAGES>
+__device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int bh, int qt, int mode, int nQT,
                                           __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+  constexpr int BMW = 32 * WAVES;
   const int hh = lane >> 5;
   const int b = bh / g.H, h = bh % g.H;
   const bool use_p = mode == SVG_TEMPORAL && !VIRT;
@@ -316,8 +375,8 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   constexpr int OE = OUT_BF16 ? 2 : 4;  // output element bytes
   auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
 
-  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nqt_of(g) + qt];
-  KVLoader<D, VIRT> ld;
+  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
+  KVLoader<D, VIRT, WAVES> ld;
   ld.init(K, V, sin.x, g.L, wave, lane);
   if (rg.y > rg.x)
     ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
@@ -325,7 +384,7 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
     ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
 
   // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
-  const int xq = qt * kBM + wave * 32 + (lane & 31);
+  const int xq = qt * BMW + wave * 32 + (lane & 31);
   const bool valid = xq < g.L;
   const int xqc = valid ? xq : g.L - 1;
   bf16x8 qf[D / 16];
@@ -334,7 +393,7 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   row_interval(g, mode, xqc, lo, hi);
 
   Flash<D> st;
-  sweep<D, VIRT>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+  sweep<D, VIRT, WAVES, STAGES>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
 
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
   const float l_tot = half_sum(st.l_part);
@@ -359,10 +418,13 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   }
 }
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT, int32_t total) {
-  using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];  // [buffer][K, V]
+template <int D, bool OUT_BF16, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 2 : 1)) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT,
+                                                                                int32_t total) {
+  using C = TileCfg<D, WAVES>;
+  constexpr int BMW = 32 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
+  auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -381,17 +443,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(KGeom g, AttnPtrs a, int32
     const int b = bh / g.H, h = bh % g.H;
     const int64_t obase = (int64_t)b * a.so.b + (int64_t)h * a.so.h;
     char* O = static_cast<char*>(a.o);
-    for (int c = tid; c < kBM * CPRO; c += 256) {
-      const int r = qt * kBM + c / CPRO;
+    for (int c = tid; c < BMW * CPRO; c += 64 * WAVES) {
+      const int r = qt * BMW + c / CPRO;
       if (r < g.L)
         *reinterpret_cast<int4*>(O + (obase + (int64_t)r * a.so.x) * OE + (c % CPRO) * 16) = make_int4(0, 0, 0, 0);
     }
     return;
   }
   if (mode == SVG_TEMPORAL && (a.flags & SVG_FLAG_VIRTUAL_PERMUTE))
-    attn_tile<D, OUT_BF16, true>(g, a, bh, qt, mode, lds, wave, lane);
+    attn_tile<D, OUT_BF16, true, WAVES, STAGES>(g, a, bh, qt, mode, nQT, lds, wave, lane);
   else
-    attn_tile<D, OUT_BF16, false>(g, a, bh, qt, mode, lds, wave, lane);
+    attn_tile<D, OUT_BF16, false, WAVES, STAGES>(g, a, bh, qt, mode, nQT, lds, wave, lane);
 }
 
 // Partial (m, l, acc) of one output of one sampled row: acc in the
@@ -553,31 +615,38 @@ __global__ __launch_bounds__(256, 2) void k_prof_temporal(KGeom g, const __bf16*
   bf16x8 qf[D / 16];
   load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
   Flash<D> st;
-  sweep<D, true>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+  sweep<D, true, 4, 2>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
     const int64_t slot = (int64_t)bh * n_rows + ord_r[rk];
     store_partial<D>(st, part_acc + slot * D, part_ml + slot * 2, hh);
   }
 }
 
+template <int D, bool OUT_BF16>
+static hipError_t launch_attn(const KGeom& g, const AttnPtrs& a, int32_t nQT, int64_t grid, int64_t total,
+                              hipStream_t st) {
+  constexpr int W = kAttnWaves, S = kAttnStages;
+  const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
+  auto kern = k_attn_bf16<D, OUT_BF16, W, S>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, a, nQT, (int32_t)total);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st) {
-  const int32_t nQT = (g.L + kBM - 1) / kBM;
+  const int32_t nQT = (g.L + kBM_bf16 - 1) / kBM_bf16;
   const int64_t total = (int64_t)g.B * g.H * nQT;
   const int64_t per_round = 8 * kXcdRun;
   const int64_t grid = (total + per_round - 1) / per_round * per_round;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  if (g.d == 64) {
-    if (out_bf16)
-      hipLaunchKernelGGL((k_attn_bf16<64, true>), dim3((unsigned)grid), dim3(256), 0, st, g, a, nQT, (int32_t)total);
-    else
-      hipLaunchKernelGGL((k_attn_bf16<64, false>), dim3((unsigned)grid), dim3(256), 0, st, g, a, nQT, (int32_t)total);
-  } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((k_attn_bf16<128, true>), dim3((unsigned)grid), dim3(256), 0, st, g, a, nQT, (int32_t)total);
-    else
-      hipLaunchKernelGGL((k_attn_bf16<128, false>), dim3((unsigned)grid), dim3(256), 0, st, g, a, nQT, (int32_t)total);
-  }
-  return hipGetLastError();
+  if (g.d == 64)
+    return out_bf16 ? launch_attn<64, true>(g, a, nQT, grid, total, st) : launch_attn<64, false>(g, a, nQT, grid, total, st);
+  return out_bf16 ? launch_attn<128, true>(g, a, nQT, grid, total, st) : launch_attn<128, false>(g, a, nQT, grid, total, st);
 }
 
 hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,

@@ -45,8 +45,9 @@ def test_python_binding_has_the_same_names():
 
 
 def test_tile_config():
-    assert svg.svg_tile_config(svg.BF16, 128) == (128, 64)
-    assert svg.svg_tile_config(svg.BF16, 64) == (128, 64)
+    bm, bn = svg.svg_tile_config(svg.BF16, 128)
+    assert bn == 64 and bm % 32 == 0 and bm >= 128
+    assert svg.svg_tile_config(svg.BF16, 64) == (bm, bn)
     assert svg.svg_tile_config(svg.F32, 64) == (64, 64)
     with pytest.raises(svg.SvgError) as e:
         svg.svg_tile_config(svg.BF16, 96)
@@ -102,8 +103,11 @@ def strides(b=4 * 64 * 128, h=64 * 128 * 0 + 256 * 128, x=128):
     return svg._Strides(b, h, x)
 
 
+BM_BF16, BN_BF16 = svg.svg_tile_config(svg.BF16, 128)
+
+
 def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, modes=A, ranges=A, order=A,
-                   BM=128, BN=64, flags=0, qp=A, sp=None):
+                   BM=BM_BF16, BN=BN_BF16, flags=0, qp=A, sp=None):
     gc = g.c()
     s = s or strides()
     so = so or strides()
