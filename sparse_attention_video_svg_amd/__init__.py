@@ -26,7 +26,8 @@ F32, BF16 = 0, 1
 VIRTUAL_PERMUTE = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsvg.so")
+# SVG_LIBRARY may point at another build of the same library (A/B timing).
+_LIB_PATH = os.environ.get("SVG_LIBRARY") or os.path.join(_HERE, "libsvg.so")
 
 
 def library_path():
@@ -79,13 +80,31 @@ class Geom:
 _lib_handle = None
 
 
+def _check_single_hip_runtime():
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise RuntimeError("two HIP runtimes are loaded in this process (" + ", ".join(sorted(real)) +
+                           "); import torch before anything that loads libamdhip64")
+
+
 def _lib():
     global _lib_handle
     if _lib_handle is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
                                "python -m sparse_attention_video_svg_amd._build")
+        # torch brings its own HIP runtime (same soname as the system one the
+        # library is linked against).  Load it first so that the library binds
+        # to that one copy: two runtimes in one process do not share devices,
+        # streams or allocations.
+        import torch  # noqa: F401
         L = ctypes.CDLL(_LIB_PATH)
+        _check_single_hip_runtime()
         P = ctypes.POINTER
         g = P(_Geom)
         S = _Strides

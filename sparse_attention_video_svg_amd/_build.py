@@ -29,7 +29,8 @@ EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"]}
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = ["hipcc", *HIP_FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra_env = os.environ.get("SVG_HIPCC_FLAGS", "").split()
+    cmd = ["hipcc", *HIP_FLAGS, *EXTRA.get(src, []), *extra_env, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -41,12 +41,14 @@ constexpr int kBN = kBN_bf16;
 constexpr float kRescaleTau = 8.0f;  // log2 headroom before the running max moves
 constexpr int kXcdRun = 32;          // consecutive query tiles per XCD turn
 
+
 template <int D, int WAVES = 4>
 struct TileCfg {
   static constexpr int CR = D / 8;                   // 16-byte chunks per row
   static constexpr int RPL = 16 / CR;                // rows per 256-byte LDS line
   static constexpr int CHUNKS = kBN * CR;            // chunks per K (or V) tile
-  static constexpr int LOADS = CHUNKS / (64 * WAVES);  // per thread per tensor
+  static constexpr int SEGS = CHUNKS / 64;                     // 64-chunk segments per tensor
+  static constexpr int LOADS = (SEGS + WAVES - 1) / WAVES;     // per thread per tensor (last may be idle)
   static constexpr int TILE_ELEMS = kBN * D;         // bf16 elements per tile
   // K rows are read 16 keys x one chunk at a time: spread keys over chunks.
   __device__ static __forceinline__ int swz_k(int r) { return (r / RPL) % CR; }
@@ -86,7 +88,7 @@ struct KVLoader {
     L = L_;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int p = (i * WAVES + wave) * 64 + lane;
+      const int p = min(i * WAVES + wave, C::SEGS - 1) * 64 + lane;
       const int r = p / C::CR, pos = p % C::CR;
       offk[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_k(r)) * 16);
       offv[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_v(r)) * 16);
@@ -102,6 +104,7 @@ struct KVLoader {
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const int seg = i * WAVES + wave;
+        if (C::SEGS % WAVES != 0 && seg >= C::SEGS) break;  // wave-uniform
         const uint32_t off = WHICH == 0 ? offk[i] : offv[i];
         __builtin_amdgcn_global_load_lds((const void*)(tb + off), (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
       }
@@ -109,6 +112,7 @@ struct KVLoader {
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const int seg = i * WAVES + wave;
+        if (C::SEGS % WAVES != 0 && seg >= C::SEGS) break;  // wave-uniform
         const int p = seg * 64 + lane;
         const int r = p / C::CR, pos = p % C::CR;
         int row = kt0 + r;
@@ -247,8 +251,9 @@ struct Flash {
       m_ref = need ? mx : m_ref;
     }
     const float nmu = m_ref == -INFINITY ? 0.f : -m_ref;
-#pragma unroll
-    for (int s16 = 0; s16 < 4; ++s16) {
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    // weights of key step s16 as bf16, their row sum folded into l_part
+    auto weights = [&](int s16) {
       f32x8 p8;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -258,12 +263,16 @@ struct Flash {
       const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
       // row sum of the bf16 weights the P.V product actually uses, two per
       // v_dot2_f32_bf16 against (1, 1)
-      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
         l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part, false);
       }
+      return pb;
+    };
+#pragma unroll
+    for (int s16 = 0; s16 < 4; ++s16) {
+      const bf16x8 pb = weights(s16);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
@@ -297,6 +306,8 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLo
                                       const KGeom& g, int4 rg, int lo, int hi, bool valid,
                                       __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
   constexpr int PER_TILE = 2 * TileCfg<D, WAVES>::LOADS;  // load instructions per tile per wave
+  static_assert(STAGES == 2 || TileCfg<D, WAVES>::SEGS % WAVES == 0,
+                "a 3-stage ring counts loads per wave: every wave must issue the same number");
   const int hh = lane >> 5;
   const int T = g.T;
   const float sl2 = g.scale_log2;
@@ -419,7 +430,7 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
 }
 
 template <int D, bool OUT_BF16, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 2 : 1)) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT,
+__global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT,
                                                                                 int32_t total) {
   using C = TileCfg<D, WAVES>;
   constexpr int BMW = 32 * WAVES;

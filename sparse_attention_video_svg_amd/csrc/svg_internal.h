@@ -80,7 +80,7 @@ hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, 
 
 // Tile sizes of the bf16 MFMA attention kernel (32 query rows per wave, a
 // ring of kAttnStages K/V tiles of 64 keys in LDS) and of the fp32 kernel.
-constexpr int32_t kAttnWaves = 8, kAttnStages = 3;
+constexpr int32_t kAttnWaves = 8, kAttnStages = 2;
 constexpr int32_t kBM_bf16 = 32 * kAttnWaves, kBN_bf16 = 64;
 constexpr int32_t kBM_f32 = 64, kBN_f32 = 64;
 // Query rows per workgroup of the bf16 profiling sweep.
