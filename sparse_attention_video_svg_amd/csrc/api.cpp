@@ -94,6 +94,8 @@ svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const ch
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
+  // key slices of each profiling sweep: enough workgroups (rows chunk x
+  // head x slice) to give every CU about four
   if (dtype != SVG_BF16) return 1;
   const int64_t chunks = (n_rows + kProfRows_bf16 - 1) / kProfRows_bf16;
   const int64_t wgs = chunks * g.B * g.H;
@@ -114,14 +116,10 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
   size_t off = 0;
   w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows) : 0;
   const size_t rows_bh = (size_t)BH * n_rows;
-  w.p1_acc = off;
-  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 2 * g.d);
-  w.p1_ml = off;
-  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 2 * 2);
-  w.p2_acc = off;
-  off = align256(off + sizeof(float) * rows_bh * g.d);
-  w.p2_ml = off;
-  off = align256(off + sizeof(float) * rows_bh * 2);
+  w.part_acc = off;
+  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 3 * g.d);
+  w.part_ml = off;
+  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 3 * 2);
   w.row_sums = off;
   off = align256(off + sizeof(double) * rows_bh * 3);
   w.ord_x = off;
@@ -224,23 +222,21 @@ svg_status validate_profile(const KGeom& g, svg_dtype dtype, const void* q, cons
 hipError_t run_profile(const KGeom& g, svg_dtype dtype, const void* q, const void* k, const void* v,
                        svg_strides s, const int32_t* rows, int32_t n_rows, float fallback, int32_t* labels,
                        float* stats, void* ws, const WsLayout& w, hipStream_t st) {
-  float* p1a = ws_at<float>(ws, w.p1_acc);
-  float* p1m = ws_at<float>(ws, w.p1_ml);
-  float* p2a = ws_at<float>(ws, w.p2_acc);
-  float* p2m = ws_at<float>(ws, w.p2_ml);
+  float* pa = ws_at<float>(ws, w.part_acc);
+  float* pm = ws_at<float>(ws, w.part_ml);
   hipError_t e;
   if (dtype == SVG_BF16) {
     int32_t* ox = ws_at<int32_t>(ws, w.ord_x);
     int32_t* orr = ws_at<int32_t>(ws, w.ord_r);
     e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
     if (e != hipSuccess) return e;
-    e = launch_profile_bf16(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, p1a, p1m, p2a, p2m, st);
+    e = launch_profile_bf16(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, pa, pm, st);
   } else {
-    e = launch_profile_f32(g, q, k, v, s, rows, n_rows, p1a, p1m, p2a, p2m, st);
+    e = launch_profile_f32(g, q, k, v, s, rows, n_rows, pa, pm, st);
   }
   if (e != hipSuccess) return e;
-  return launch_profile_merge(g, n_rows, w.ksplit, dtype == SVG_BF16 ? 0 : 1, p1a, p1m, p2a, p2m,
-                              ws_at<double>(ws, w.row_sums), fallback, labels, stats, st);
+  return launch_profile_merge(g, n_rows, w.ksplit, pa, pm, ws_at<double>(ws, w.row_sums), fallback, labels, stats,
+                              st);
 }
 
 }  // namespace

@@ -487,149 +487,114 @@ __device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, fl
 }
 
 // ---------------------------------------------------------------------------
-// Profiling, sweep 1 (frame-major keys): full and spatial attention of the
-// sampled rows.  Each key goes to exactly one of two online-softmax states,
-// IN (the row's spatial keys: its frame run and the text prefix) and OUT (all
-// other keys), so the tile's P.V is computed once; the merge then gives
-// O_spatial = IN and O_full = IN combined with OUT.  A workgroup takes 128
-// sampled rows (4 waves x 32) of one head and one of `ksplit` slices of the
-// key tiles.
-template <int D>
-__global__ __launch_bounds__(256, 1) void k_prof_spatial(KGeom g, const __bf16* __restrict__ q,
-                                                         const __bf16* __restrict__ k,
-                                                         const __bf16* __restrict__ v, svg_strides s,
-                                                         const int32_t* __restrict__ rows, int32_t n_rows,
-                                                         int32_t ksplit, float* __restrict__ part_acc,
-                                                         float* __restrict__ part_ml) {
-  using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];
+// Profiling sweeps: the full, spatial and temporal attention of the sampled
+// rows, each a single online-softmax state swept by the same machinery as the
+// attention kernel (8 waves x 32 rows, K/V ring in LDS).
+//   PROF_FULL      every key; the key tiles are cut into `ksplit` slices so
+//                  that the grid fills the chip, the merge combines them.
+//   PROF_SPATIAL   the row's frame run and the text prefix (frame-major keys);
+//                  the rows are ascending, so a workgroup's runs are close
+//                  and it loads only their union.
+//   PROF_TEMPORAL  the row's position band and the text prefix, with keys
+//                  gathered in token-major order through the index map and
+//                  the rows taken in position order (k_prof_rank), so again a
+//                  workgroup loads only the union of its bands.
+// Waves skip the tiles none of their rows needs.  Workgroup ids are remapped
+// so that the chunks of rows sharing one key slice of one head run together
+// on one XCD and share those K/V tiles in its L2.
+enum : int { PROF_FULL = 0, PROF_SPATIAL = 1, PROF_TEMPORAL = 2 };
+
+template <int D, int KIND, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep(
+    KGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    svg_strides s, const int32_t* __restrict__ rows, const int32_t* __restrict__ ord_r, int32_t n_rows,
+    int32_t nsplit, int32_t total, float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  using C = TileCfg<D, WAVES>;
+  constexpr bool VIRT = KIND == PROF_TEMPORAL;
+  constexpr int BMW = 32 * WAVES;
+  constexpr int KIND_STATE = KIND == PROF_SPATIAL ? 0 : (KIND == PROF_FULL ? 1 : 2);
+  extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
+  auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
+  __shared__ int wb[2][WAVES];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = blockIdx.x, split = blockIdx.y, bh = blockIdx.z;
+
+  const int w = blockIdx.x;
+  const int xcd = w & 7, slot = w >> 3;
+  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  if (logical >= total) return;
+  const int chunks = (n_rows + BMW - 1) / BMW;
+  const int chunk = logical % chunks;
+  const int split = (logical / chunks) % nsplit, bh = logical / chunks / nsplit;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  KVLoader<D, false> ld;
-  ld.init(k + base, v + base, s.x, g.L, wave, lane);
 
-  const int nKT = (g.L + kBN - 1) / kBN;
-  const int t_begin = (int)((int64_t)nKT * split / ksplit), t_end = (int)((int64_t)nKT * (split + 1) / ksplit);
-  const int nt = t_end - t_begin;
-  if (nt > 0) ld.load(g, t_begin * kBN, lds[0][0], lds[0][1], wave, lane);
-
-  const int ridx = chunk * kProfRows_bf16 + wave * 32 + (lane & 31);
-  const bool valid = ridx < n_rows;
-  const int x = rows[valid ? ridx : n_rows - 1];
-  bf16x8 qf[D / 16];
-  load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
-  // spatial run [slo, shi) of whole frames (text keys are IN as well)
-  const int u = x - g.T;
-  const int fi = fastdiv(u, g.divF_mul, g.divF_shift);
-  const int slo = g.T + max(0, fi - g.a1 + 1) * g.F, shi = g.T + min(g.N, fi + g.a1) * g.F;
-  const int max_slo = wave_max_i(valid ? slo : INT_MIN), min_shi = wave_min_i(valid ? shi : INT_MAX);
-  const int min_slo = wave_min_i(valid ? slo : INT_MAX), max_shi = wave_max_i(valid ? shi : INT_MIN);
-  const float sl2 = g.scale_log2;
-
-  Flash<D> in_st, out_st;
-  in_st.init();
-  out_st.init();
-  wait_vm_all();
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int bf = t & 1;
-    if (t + 1 < nt)
-      ld.load(g, (t_begin + t + 1) * kBN, lds[bf ^ 1][0], lds[bf ^ 1][1], wave, lane);
-    const int kt0 = (t_begin + t) * kBN, kt1 = kt0 + kBN;
-    const __bf16* lk = lds[bf][0];
-    const __bf16* lv = lds[bf][1];
-    f32x16 s0 = score_block<D>(lk, qf, 0, lane);
-    f32x16 s1 = score_block<D>(lk, qf, 1, lane);
-    const bool all_in = kt1 <= g.T || (kt0 >= max_slo && kt1 <= min_shi);
-    const bool all_out = kt0 >= g.T && kt1 <= g.L && (kt1 <= min_slo || kt0 >= max_shi);
-    if (all_in) {
-      in_st.add_tile(s0, s1, lv, lane, sl2);
-    } else if (all_out) {
-      out_st.add_tile(s0, s1, lv, lane, sl2);
-    } else {
-      f32x16 i0 = s0, i1 = s1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k0 = kt0 + acc_key(0, r, hh), k1 = kt0 + acc_key(1, r, hh);
-        const bool in0 = k0 < g.T || (k0 >= slo && k0 < shi), in1 = k1 < g.T || (k1 >= slo && k1 < shi);
-        i0[r] = in0 ? s0[r] : -INFINITY;
-        i1[r] = in1 ? s1[r] : -INFINITY;
-        s0[r] = (in0 || k0 >= g.L) ? -INFINITY : s0[r];
-        s1[r] = (in1 || k1 >= g.L) ? -INFINITY : s1[r];
-      }
-      in_st.add_tile(i0, i1, lv, lane, sl2);
-      out_st.add_tile(s0, s1, lv, lane, sl2);
-    }
-    wait_vm_all();
-    __syncthreads();
-  }
-  if (valid) {
-    const int64_t slot = (((int64_t)bh * n_rows + ridx) * ksplit + split) * 2;
-    store_partial<D>(in_st, part_acc + slot * D, part_ml + slot * 2, hh);
-    store_partial<D>(out_st, part_acc + (slot + 1) * D, part_ml + (slot + 1) * 2, hh);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Profiling, sweep 2 (token-major keys): temporal attention of the sampled
-// rows.  In token-major order a row's temporal keys are one band (plus the
-// text prefix), so with the rows taken in order of their position j (the
-// order from k_prof_rank) a workgroup's 128 rows need only the union of
-// their bands.  K and V rows are gathered through the index map; queries are
-// read in place.
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_prof_temporal(KGeom g, const __bf16* __restrict__ q,
-                                                          const __bf16* __restrict__ k,
-                                                          const __bf16* __restrict__ v, svg_strides s,
-                                                          const int32_t* __restrict__ ord_x,
-                                                          const int32_t* __restrict__ ord_r, int32_t n_rows,
-                                                          float* __restrict__ part_acc, float* __restrict__ part_ml) {
-  using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][C::TILE_ELEMS];
-  __shared__ int wb[2][4];
-  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / g.H, h = bh % g.H;
-  const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  KVLoader<D, true> ld;
-  ld.init(k + base, v + base, s.x, g.L, wave, lane);
-
-  const int rk = chunk * kProfRows_bf16 + wave * 32 + (lane & 31);
+  const int rk = chunk * BMW + wave * 32 + (lane & 31);
   const bool valid = rk < n_rows;
-  const int x = ord_x[valid ? rk : n_rows - 1];
+  const int x = rows[valid ? rk : n_rows - 1];
   const int u = x - g.T;
-  const int j = u - fastdiv(u, g.divF_mul, g.divF_shift) * g.F;
-  const int lo = g.T + max(0, j - g.a2 + 1) * g.N, hi = g.T + min(g.F, j + g.a2) * g.N;
-  // workgroup's band union -> tile ranges (text tiles first)
-  const int wlo = wave_min_i(valid ? lo : INT_MAX), whi = wave_max_i(valid ? hi : INT_MIN);
-  if (lane == 0) {
-    wb[0][wave] = wlo;
-    wb[1][wave] = whi;
-  }
-  __syncthreads();
-  const int ulo = min(min(wb[0][0], wb[0][1]), min(wb[0][2], wb[0][3]));
-  const int uhi = max(max(wb[1][0], wb[1][1]), max(wb[1][2], wb[1][3]));
-  const int bs = ulo / kBN, be = (uhi + kBN - 1) / kBN, te = (g.T + kBN - 1) / kBN;
+  const int fi = fastdiv(u, g.divF_mul, g.divF_shift), j = u - fi * g.F;
+  int lo, hi;
   int4 rg;
-  if (g.T == 0)
-    rg = make_int4(bs, be, 0, 0);
-  else if (te >= bs)
-    rg = make_int4(0, max(be, te), 0, 0);
-  else
-    rg = make_int4(0, te, bs, be);
-  ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
+  if (KIND == PROF_FULL) {
+    lo = 0;
+    hi = g.L;
+    const int nKT = (g.L + kBN - 1) / kBN;
+    rg = make_int4((int)((int64_t)nKT * split / nsplit), (int)((int64_t)nKT * (split + 1) / nsplit), 0, 0);
+  } else {
+    if (KIND == PROF_SPATIAL) {
+      lo = g.T + max(0, fi - g.a1 + 1) * g.F;
+      hi = g.T + min(g.N, fi + g.a1) * g.F;
+    } else {
+      lo = g.T + max(0, j - g.a2 + 1) * g.N;
+      hi = g.T + min(g.F, j + g.a2) * g.N;
+    }
+    // the workgroup's union of runs -> tile ranges (text tiles first)
+    const int wlo = wave_min_i(valid ? lo : INT_MAX), whi = wave_max_i(valid ? hi : INT_MIN);
+    if (lane == 0) {
+      wb[0][wave] = wlo;
+      wb[1][wave] = whi;
+    }
+    __syncthreads();
+    int ulo = wb[0][0], uhi = wb[1][0];
+#pragma unroll
+    for (int i = 1; i < WAVES; ++i) {
+      ulo = min(ulo, wb[0][i]);
+      uhi = max(uhi, wb[1][i]);
+    }
+    const int bs = ulo / kBN, be = (uhi + kBN - 1) / kBN, te = (g.T + kBN - 1) / kBN;
+    int4 u4;
+    if (g.T == 0)
+      u4 = make_int4(bs, be, 0, 0);
+    else if (te >= bs)
+      u4 = make_int4(0, max(be, te), 0, 0);
+    else
+      u4 = make_int4(0, te, bs, be);
+    // this workgroup's slice of the concatenated tile sequence
+    const int n1 = u4.y - u4.x, nt = n1 + (u4.w - u4.z);
+    const int t0 = (int)((int64_t)nt * split / nsplit), t1 = (int)((int64_t)nt * (split + 1) / nsplit);
+    rg.x = u4.x + min(t0, n1);
+    rg.y = u4.x + min(t1, n1);
+    rg.z = u4.z + max(t0 - n1, 0);
+    rg.w = u4.z + max(t1 - n1, 0);
+  }
+  KVLoader<D, VIRT, WAVES> ld;
+  ld.init(k + base, v + base, s.x, g.L, wave, lane);
+  if (rg.y > rg.x)
+    ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
+  else if (rg.w > rg.z)
+    ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
 
   bf16x8 qf[D / 16];
   load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
   Flash<D> st;
-  sweep<D, true, 4, 2>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+  sweep<D, VIRT, WAVES, STAGES>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
-    const int64_t slot = (int64_t)bh * n_rows + ord_r[rk];
-    store_partial<D>(st, part_acc + slot * D, part_ml + slot * 2, hh);
+    // slot (row, slice, state): state 0 spatial, 1 full, 2 temporal; the
+    // temporal sweep's rows come in position order, ord_r maps them back
+    const int r = KIND == PROF_TEMPORAL ? ord_r[rk] : rk;
+    const int64_t o = (((int64_t)bh * n_rows + r) * nsplit + split) * 3 + KIND_STATE;
+    store_partial<D>(st, part_acc + o * D, part_ml + o * 2, hh);
   }
 }
 
@@ -660,26 +625,47 @@ hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf1
   return out_bf16 ? launch_attn<128, true>(g, a, nQT, grid, total, st) : launch_attn<128, false>(g, a, nQT, grid, total, st);
 }
 
+template <int D, int KIND>
+static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
+                              const int32_t* rows, const int32_t* ord_r, int32_t n_rows, int32_t nsplit,
+                              float* acc, float* ml, hipStream_t st) {
+  constexpr int W = kAttnWaves, S = kAttnStages;
+  const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
+  auto kern = k_prof_sweep<D, KIND, W, S>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t chunks = (n_rows + 32 * W - 1) / (32 * W);
+  const int64_t total = chunks * nsplit * g.B * g.H;
+  const int64_t per_round = 8 * kXcdRun;
+  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, q, k, v, s, rows, ord_r, n_rows, nsplit,
+                     (int32_t)total, acc, ml);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prof_all(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
+                                  const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                                  const int32_t* ord_r, float* acc, float* ml, hipStream_t st) {
+  hipError_t e = launch_prof<D, PROF_FULL>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, acc, ml, st);
+  if (e != hipSuccess) return e;
+  e = launch_prof<D, PROF_SPATIAL>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, acc, ml, st);
+  if (e != hipSuccess) return e;
+  return launch_prof<D, PROF_TEMPORAL>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, acc, ml, st);
+}
+
 hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
                                const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
-                               const int32_t* ord_r, float* p1_acc, float* p1_ml, float* p2_acc, float* p2_ml,
-                               hipStream_t st) {
-  const unsigned chunks = (unsigned)((n_rows + kProfRows_bf16 - 1) / kProfRows_bf16);
-  const unsigned BH = (unsigned)(g.B * g.H);
+                               const int32_t* ord_r, float* acc, float* ml, hipStream_t st) {
   const __bf16 *bq = static_cast<const __bf16*>(q), *bk = static_cast<const __bf16*>(k),
                *bv = static_cast<const __bf16*>(v);
-  if (g.d == 64) {
-    hipLaunchKernelGGL(k_prof_spatial<64>, dim3(chunks, (unsigned)ksplit, BH), dim3(256), 0, st, g, bq, bk, bv, s,
-                       rows, n_rows, ksplit, p1_acc, p1_ml);
-    hipLaunchKernelGGL(k_prof_temporal<64>, dim3(chunks, BH), dim3(256), 0, st, g, bq, bk, bv, s, ord_x, ord_r,
-                       n_rows, p2_acc, p2_ml);
-  } else {
-    hipLaunchKernelGGL(k_prof_spatial<128>, dim3(chunks, (unsigned)ksplit, BH), dim3(256), 0, st, g, bq, bk, bv, s,
-                       rows, n_rows, ksplit, p1_acc, p1_ml);
-    hipLaunchKernelGGL(k_prof_temporal<128>, dim3(chunks, BH), dim3(256), 0, st, g, bq, bk, bv, s, ord_x, ord_r,
-                       n_rows, p2_acc, p2_ml);
-  }
-  return hipGetLastError();
+  if (g.d == 64) return launch_prof_all<64>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, acc, ml, st);
+  return launch_prof_all<128>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, acc, ml, st);
 }
 
 }  // namespace svg

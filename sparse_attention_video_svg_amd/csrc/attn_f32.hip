@@ -103,9 +103,8 @@ template <int D>
 __global__ __launch_bounds__(64) void k_profile_f32(KGeom g, const float* __restrict__ q,
                                                     const float* __restrict__ k, const float* __restrict__ v,
                                                     svg_strides s, const int32_t* __restrict__ rows,
-                                                    int32_t n_rows, float* __restrict__ p1_acc,
-                                                    float* __restrict__ p1_ml, float* __restrict__ p2_acc,
-                                                    float* __restrict__ p2_ml) {
+                                                    int32_t n_rows, float* __restrict__ part_acc,
+                                                    float* __restrict__ part_ml) {
   __shared__ float qs[D];
   __shared__ double ps[3][64];
   const int lane = threadIdx.x;
@@ -174,12 +173,11 @@ __global__ __launch_bounds__(64) void k_profile_f32(KGeom g, const float* __rest
     }
     __syncthreads();
   }
-  // Outputs already normalised (l = 1, m = 0): sweep-1 slots hold the
-  // spatial (state 0) and the full output (state 1, merged with full_direct),
-  // the sweep-2 slot holds the temporal output.
+  // Outputs already normalised (l = 1, m = 0), one key slice: state 0 the
+  // spatial, 1 the full, 2 the temporal output.
   const int64_t row = (int64_t)bh * n_rows + r;
-  float* dst_acc[3] = {p1_acc + (row * 2 + 0) * D, p1_acc + (row * 2 + 1) * D, p2_acc + row * D};
-  float* dst_ml[3] = {p1_ml + (row * 2 + 0) * 2, p1_ml + (row * 2 + 1) * 2, p2_ml + row * 2};
+  float* dst_acc[3] = {part_acc + (row * 3 + 0) * D, part_acc + (row * 3 + 1) * D, part_acc + (row * 3 + 2) * D};
+  float* dst_ml[3] = {part_ml + (row * 3 + 0) * 2, part_ml + (row * 3 + 1) * 2, part_ml + (row * 3 + 2) * 2};
   const int which[3] = {1, 0, 2};  // destination of full, spatial, temporal
 #pragma unroll
   for (int st = 0; st < 3; ++st) {
@@ -205,17 +203,17 @@ hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, i
 }
 
 hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                              const int32_t* rows, int32_t n_rows, float* p1_acc, float* p1_ml, float* p2_acc,
-                              float* p2_ml, hipStream_t st) {
+                              const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml,
+                              hipStream_t st) {
   dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
   const float *fq = static_cast<const float*>(q), *fk = static_cast<const float*>(k),
               *fv = static_cast<const float*>(v);
   if (g.d == 64)
-    hipLaunchKernelGGL(k_profile_f32<64>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, p1_acc, p1_ml,
-                       p2_acc, p2_ml);
+    hipLaunchKernelGGL(k_profile_f32<64>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, part_acc,
+                       part_ml);
   else
-    hipLaunchKernelGGL(k_profile_f32<128>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, p1_acc, p1_ml,
-                       p2_acc, p2_ml);
+    hipLaunchKernelGGL(k_profile_f32<128>, grid, dim3(64), 0, st, g, fq, fk, fv, s, rows, n_rows, part_acc,
+                       part_ml);
   return hipGetLastError();
 }
 

@@ -6,11 +6,10 @@
 // and the temporal mask on the sampled rows:
 //   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
 //   label = SPATIAL if rel_s <= rel_t else TEMPORAL, FULL if min >= fallback.
-// Sweep 1 leaves per row and key slice two partial states (m in log2 units,
-// l, unnormalised acc): IN (spatial keys) and OUT (the rest), or, with
-// full_direct, the spatial and the full output themselves; sweep 2 leaves the
-// temporal state.  Rows are merged in parallel, each row's three squared-error
-// sums are written, and one workgroup per head adds them in a fixed order.
+// The sweeps leave per row and key slice three partial states (m in log2
+// units, l, unnormalised acc): spatial, full and temporal.  Rows are merged in
+// parallel, each row's three squared-error sums are written, and one
+// workgroup per head adds them in a fixed order.
 #include "svg_device.h"
 
 namespace svg {
@@ -49,42 +48,32 @@ __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n
   ord_r[rank] = r;
 }
 
-// One workgroup (D threads, one per dim) per (sampled row, head).
+// One workgroup (D threads, one per dim) per (sampled row, head): each of
+// the three states merged over the key slices, then normalised.
 template <int D>
-__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit, int32_t full_direct,
-                                                       const float* __restrict__ p1_acc,
-                                                       const float* __restrict__ p1_ml,
-                                                       const float* __restrict__ p2_acc,
-                                                       const float* __restrict__ p2_ml, double* __restrict__ row_sums) {
+__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit,
+                                                       const float* __restrict__ part_acc,
+                                                       const float* __restrict__ part_ml,
+                                                       double* __restrict__ row_sums) {
   const int r = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
   const int64_t row = (int64_t)bh * n_rows + r;
-  // states 0 and 1 of sweep 1, merged over the key slices
-  float m[2] = {-INFINITY, -INFINITY};
-  for (int s = 0; s < ksplit; ++s)
+  float o[3];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) m[st] = fmaxf(m[st], p1_ml[((row * ksplit + s) * 2 + st) * 2]);
-  float l[2] = {0.f, 0.f}, a[2] = {0.f, 0.f};
-  for (int s = 0; s < ksplit; ++s)
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (m[st] == -INFINITY) continue;
-      const int64_t slot = (row * ksplit + s) * 2 + st;
-      const float w = exp2f(p1_ml[slot * 2] - m[st]);
-      l[st] += w * p1_ml[slot * 2 + 1];
-      a[st] += w * p1_acc[slot * D + c];
+  for (int st = 0; st < 3; ++st) {
+    float m = -INFINITY;
+    for (int s = 0; s < ksplit; ++s) m = fmaxf(m, part_ml[((row * ksplit + s) * 3 + st) * 2]);
+    float l = 0.f, a = 0.f;
+    if (m != -INFINITY) {
+      for (int s = 0; s < ksplit; ++s) {
+        const int64_t slot = (row * ksplit + s) * 3 + st;
+        const float w = exp2f(part_ml[slot * 2] - m);
+        l += w * part_ml[slot * 2 + 1];
+        a += w * part_acc[slot * D + c];
+      }
     }
-  const float o_sp = l[0] > 0.f ? a[0] / l[0] : 0.f;
-  float o_f;
-  if (full_direct) {
-    o_f = l[1] > 0.f ? a[1] / l[1] : 0.f;
-  } else {  // full = IN combined with OUT
-    const float mm = fmaxf(m[0], m[1]);
-    const float w0 = m[0] == -INFINITY ? 0.f : exp2f(m[0] - mm), w1 = m[1] == -INFINITY ? 0.f : exp2f(m[1] - mm);
-    const float lf = l[0] * w0 + l[1] * w1;
-    o_f = lf > 0.f ? (a[0] * w0 + a[1] * w1) / lf : 0.f;
+    o[st] = l > 0.f ? a / l : 0.f;
   }
-  const float lt = p2_ml[row * 2 + 1];
-  const float o_tp = lt > 0.f ? p2_acc[row * D + c] / lt : 0.f;
+  const float o_sp = o[0], o_f = o[1], o_tp = o[2];
   const double ds = (double)o_sp - (double)o_f, dt = (double)o_tp - (double)o_f;
   __shared__ double red[3][D];
   red[0][c] = ds * ds;
@@ -139,16 +128,14 @@ hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_ro
   return hipGetLastError();
 }
 
-hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t full_direct,
-                                const float* p1_acc, const float* p1_ml, const float* p2_acc, const float* p2_ml,
-                                double* row_sums, float fallback, int32_t* labels, float* stats, hipStream_t st) {
+hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
+                                const float* part_ml, double* row_sums, float fallback, int32_t* labels, float* stats,
+                                hipStream_t st) {
   dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
   if (g.d == 64)
-    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, full_direct, p1_acc, p1_ml,
-                       p2_acc, p2_ml, row_sums);
+    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, part_acc, part_ml, row_sums);
   else
-    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, full_direct, p1_acc, p1_ml,
-                       p2_acc, p2_ml, row_sums);
+    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, part_acc, part_ml, row_sums);
   hipLaunchKernelGGL(k_prof_finalize, dim3((unsigned)(g.B * g.H)), dim3(256), 0, st, g.d, n_rows, row_sums, fallback,
                      labels, stats);
   return hipGetLastError();

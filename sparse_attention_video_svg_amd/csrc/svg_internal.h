@@ -39,7 +39,7 @@ __device__ __forceinline__ int32_t fastdiv(int32_t n, uint32_t mul, uint32_t shi
 
 // Workspace carve-up for svg_layer_forward / svg_profile_heads.
 struct WsLayout {
-  size_t p1_acc, p1_ml, p2_acc, p2_ml, row_sums, ord_x, ord_r;  // profiling
+  size_t part_acc, part_ml, row_sums, ord_x, ord_r;  // profiling
   size_t labels, ranges, order, perm, total;
   size_t perm_tensor_bytes;  // one permuted tensor (all heads)
   int32_t ksplit;            // key splits of the profiling sweep
@@ -61,29 +61,27 @@ struct AttnPtrs {
 hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, int32_t BN, hipStream_t st);
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st);
 
-// Profiling: sweep 1 (frame-major keys) writes per (head, row, key slice)
-// two partial states (m, l, acc); sweep 2 (token-major keys, rows in position
-// order) writes the temporal state; the merge reduces them, deterministically,
-// into labels and stats.
+// Profiling: the sweeps write, per (head, row, key slice), three partial
+// online-softmax states (m in log2 units, l, unnormalised acc): 0 spatial,
+// 1 full, 2 temporal, at slot ((bh * n_rows + row) * ksplit + slice) * 3 +
+// state.  The merge reduces them, deterministically, into labels and stats.
 hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
                                hipStream_t st);
 hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                              const int32_t* rows, int32_t n_rows, float* p1_acc, float* p1_ml, float* p2_acc,
-                              float* p2_ml, hipStream_t st);
+                              const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml, hipStream_t st);
 hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
                                const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
-                               const int32_t* ord_r, float* p1_acc, float* p1_ml, float* p2_acc, float* p2_ml,
-                               hipStream_t st);
-hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t full_direct,
-                                const float* p1_acc, const float* p1_ml, const float* p2_acc, const float* p2_ml,
-                                double* row_sums, float fallback, int32_t* labels, float* stats, hipStream_t st);
+                               const int32_t* ord_r, float* part_acc, float* part_ml, hipStream_t st);
+hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
+                                const float* part_ml, double* row_sums, float fallback, int32_t* labels, float* stats,
+                                hipStream_t st);
 
 // Tile sizes of the bf16 MFMA attention kernel (32 query rows per wave, a
 // ring of kAttnStages K/V tiles of 64 keys in LDS) and of the fp32 kernel.
 constexpr int32_t kAttnWaves = 8, kAttnStages = 2;
 constexpr int32_t kBM_bf16 = 32 * kAttnWaves, kBN_bf16 = 64;
 constexpr int32_t kBM_f32 = 64, kBN_f32 = 64;
-// Query rows per workgroup of the bf16 profiling sweep.
-constexpr int32_t kProfRows_bf16 = 128;
+// Query rows per workgroup of the bf16 profiling sweeps.
+constexpr int32_t kProfRows_bf16 = kBM_bf16;
 
 }  // namespace svg
