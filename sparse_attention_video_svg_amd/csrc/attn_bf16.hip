@@ -7,10 +7,10 @@
 // Sparse-vDiT review for the per-mode kernels with heads of one mode fused).
 //
 // How (MI355X-first):
-//  * A workgroup is 4 waves x 32 query rows (BM = 128) and walks its key-tile
+//  * A workgroup is 8 waves x 32 query rows (BM = 256) and walks its key-tile
 //    ranges in tiles of BN = 64 keys.  K and V tiles are fetched straight
 //    into LDS with global_load_lds_dwordx4 (no VGPR staging), double
-//    buffered, one barrier per tile.
+//    buffered, one barrier per tile; two waves share each SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: Q stays in registers as the B operand, each
 //    lane then owns one query and 16 keys per 32-key block, so the row max and
@@ -234,9 +234,10 @@ struct Flash {
   }
 
   // s0, s1: raw scores of the two 32-key blocks of a tile, masked entries
-  // already -inf.  sl2 = scale * log2(e) > 0.
-  __device__ __forceinline__ void add_tile(const f32x16& s0, const f32x16& s1, const __bf16* lv, int lane,
-                                           float sl2) {
+  // already -inf.  sl2 = scale * log2(e) > 0.  Leaves the tile's weights as
+  // bf16 in pbs (key step s16 = 16 keys each) and folds their row sum into
+  // l_part; rescales o when the reference max moves.
+  __device__ __forceinline__ void softmax(const f32x16& s0, const f32x16& s1, float sl2, bf16x8* pbs) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -252,8 +253,8 @@ struct Flash {
     }
     const float nmu = m_ref == -INFINITY ? 0.f : -m_ref;
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    // weights of key step s16 as bf16, their row sum folded into l_part
-    auto weights = [&](int s16) {
+#pragma unroll
+    for (int s16 = 0; s16 < 4; ++s16) {
       f32x8 p8;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -268,17 +269,27 @@ struct Flash {
         const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
         l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part, false);
       }
-      return pb;
-    };
+      pbs[s16] = pb;
+    }
+  }
+
+  // o += P V for the weights of one tile; V^T fragments read from LDS.
+  __device__ __forceinline__ void pv(const bf16x8* pbs, const __bf16* lv, int lane) {
 #pragma unroll
     for (int s16 = 0; s16 < 4; ++s16) {
-      const bf16x8 pb = weights(s16);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const bf16x8 vf = v_fragment<D>(lv, s16, db, lane);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pbs[s16], o[db], 0, 0, 0);
       }
     }
+  }
+
+  __device__ __forceinline__ void add_tile(const f32x16& s0, const f32x16& s1, const __bf16* lv, int lane,
+                                           float sl2) {
+    bf16x8 pbs[4];
+    softmax(s0, s1, sl2, pbs);
+    pv(pbs, lv, lane);
   }
 };
 
@@ -358,6 +369,21 @@ __device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLo
   }
 }
 
+
+// Sweep of one workgroup's tile ranges into st.
+template <int D, bool VIRT, int WAVES, int STAGES>
+__device__ __forceinline__ void run_sweep(Flash<D>& st, const bf16x8* qf, const __bf16* K, const __bf16* V, int64_t sx,
+                                          const KGeom& g, int4 rg, int lo, int hi, bool valid,
+                                          __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
+  KVLoader<D, VIRT, WAVES> ld;
+  ld.init(K, V, sx, g.L, wave, lane);
+  if (rg.y > rg.x)
+    ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
+  else if (rg.w > rg.z)
+    ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
+  sweep<D, VIRT, WAVES, STAGES>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+}
+
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8* qf, const __bf16* qrow_base, int hh) {
   const __bf16* qrow = qrow_base + 8 * hh;
@@ -387,12 +413,6 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
 
   const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
-  KVLoader<D, VIRT, WAVES> ld;
-  ld.init(K, V, sin.x, g.L, wave, lane);
-  if (rg.y > rg.x)
-    ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
-  else if (rg.w > rg.z)
-    ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
 
   // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
   const int xq = qt * BMW + wave * 32 + (lane & 31);
@@ -404,7 +424,7 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   row_interval(g, mode, xqc, lo, hi);
 
   Flash<D> st;
-  sweep<D, VIRT, WAVES, STAGES>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+  run_sweep<D, VIRT, WAVES, STAGES>(st, qf, K, V, sin.x, g, rg, lo, hi, valid, lds, wave, lane);
 
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
   const float l_tot = half_sum(st.l_part);
@@ -578,17 +598,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
     rg.z = u4.z + max(t0 - n1, 0);
     rg.w = u4.z + max(t1 - n1, 0);
   }
-  KVLoader<D, VIRT, WAVES> ld;
-  ld.init(k + base, v + base, s.x, g.L, wave, lane);
-  if (rg.y > rg.x)
-    ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
-  else if (rg.w > rg.z)
-    ld.load(g, rg.z * kBN, lds[0][0], lds[0][1], wave, lane);
-
   bf16x8 qf[D / 16];
   load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
   Flash<D> st;
-  sweep<D, VIRT, WAVES, STAGES>(st, qf, ld, g, rg, lo, hi, valid, lds, wave, lane);
+  run_sweep<D, VIRT, WAVES, STAGES>(st, qf, k + base, v + base, s.x, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
     // slot (row, slice, state): state 0 spatial, 1 full, 2 temporal; the
     // temporal sweep's rows come in position order, ord_r maps them back
