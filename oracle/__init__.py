@@ -68,6 +68,11 @@ def lib():
         L.og_profile_head.argtypes = [g, ctypes.c_int32, ctypes.c_double, vp, vp, vp, vp, ctypes.c_int64,
                                       ctypes.c_double, vp, vp]
         L.og_profile_head.restype = None
+        L.og_mask_nnz.argtypes = [g, ctypes.c_int]
+        L.og_mask_nnz.restype = ctypes.c_int64
+        L.og_search_head.argtypes = [g, ctypes.c_int32, ctypes.c_double, vp, vp, vp, vp, ctypes.c_int64,
+                                     ctypes.c_double, ctypes.c_double, ctypes.c_int, vp, vp, vp, vp]
+        L.og_search_head.restype = None
         L.og_blocks_brute.argtypes = [g, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, vp]
         L.og_blocks_brute.restype = None
         L.og_blocks_rows.argtypes = [g, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, vp]
@@ -167,6 +172,27 @@ def profile_head(g, q, k, v, scale, rows, fallback=0.05):
     lib().og_profile_head(ctypes.byref(g), q.shape[1], float(scale), _ptr(q), _ptr(k), _ptr(v),
                           _ptr(rows), rows.shape[0], float(fallback), _ptr(stats), _ptr(label))
     return int(label[0]), stats
+
+
+def mask_nnz(g, mode):
+    """Active (query, key) pairs of a mask over the whole map."""
+    return int(lib().og_mask_nnz(ctypes.byref(g), mode))
+
+
+SEARCH_CANDIDATES = (SKIP, WINDOW, TEMPORAL, STRIPE)
+
+
+def search_head(g, q, k, v, scale, rows, lam=0.5, eps=1.0, penalty=0):
+    """Sparse-vDiT mode search of one head.  Returns (mode, mse[4], loss[4],
+    sparsity[4]) with the candidates in SEARCH_CANDIDATES order."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    mse, loss, sp = (np.zeros(4, dtype=np.float64) for _ in range(3))
+    mode = np.zeros(1, dtype=np.int32)
+    lib().og_search_head(ctypes.byref(g), q.shape[1], float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(rows),
+                         rows.shape[0], float(lam), float(eps), int(penalty), _ptr(mse), _ptr(loss), _ptr(sp),
+                         _ptr(mode))
+    return int(mode[0]), mse, loss, sp
 
 
 def blocks(g, mode, BM, BN, brute=False):

@@ -318,6 +318,64 @@ void og_profile_head(const og_geom* g, int32_t d, double scale, const float* q, 
   free(ot);
 }
 
+/* Number of active (query, key) pairs of a mask over the whole L x L map,
+ * summed from the per-row intervals (tests pin it to the literal predicate
+ * counted pair by pair).  SKIP has none. */
+int64_t og_mask_nnz(const og_geom* g, int mode) {
+  int64_t L = og_ltot(g), total = 0;
+#pragma omp parallel for reduction(+ : total) schedule(static)
+  for (int64_t x1 = 0; x1 < L; ++x1) {
+    int64_t lo[4100], hi[4100];
+    int ni = og_row_intervals(g, mode, x1, lo, hi, 4100);
+    for (int t = 0; t < ni; ++t) total += hi[t] - lo[t];
+  }
+  return total;
+}
+
+/* Offline mode search of one head ("Sparse-vDiT" review: the search scores
+ * each candidate mode's output against full attention by mean squared error
+ * plus a sparsity penalty, and keeps full attention when every candidate is
+ * above the threshold; the referee report quotes Eq. (2) with the penalty
+ * lam*(1 - S_i) and Algorithm 1 with lam*S_i).
+ * Candidates, in this order (ties go to the earlier one): skip (O = 0,
+ * S = 1), diagonal (WINDOW), multi-diagonal (TEMPORAL band), vertical stripe
+ * (STRIPE).  S_i = 1 - nnz_i / L^2 is the fraction of the map a mode skips.
+ *   mse_i  = mean over rows x d of (O_i - O_full)^2
+ *   loss_i = mse_i + lam * (1 - S_i)   (penalty 0)   or   mse_i + lam * S_i   (penalty 1)
+ * mode = the candidate with the lowest loss, or FULL if every loss > eps.
+ * mse[4], loss[4], sparsity[4] in candidate order. */
+void og_search_head(const og_geom* g, int32_t d, double scale, const float* q, const float* k,
+                    const float* v, const int64_t* rows, int64_t n_rows, double lam, double eps,
+                    int penalty, double* mse, double* loss, double* sparsity, int32_t* mode) {
+  static const int cand[4] = {OG_SKIP, OG_WINDOW, OG_TEMPORAL, OG_STRIPE};
+  size_t n = (size_t)n_rows * (size_t)d;
+  double L = (double)og_ltot(g);
+  double* of = (double*)malloc(sizeof(double) * n);
+  double* om = (double*)malloc(sizeof(double) * n);
+  og_attention_rows(g, OG_FULL, d, scale, q, k, v, rows, n_rows, of);
+  int best = -1;
+  for (int c = 0; c < 4; ++c) {
+    double se = 0.0;
+    if (cand[c] == OG_SKIP) {
+      for (size_t e = 0; e < n; ++e) se += of[e] * of[e];
+      sparsity[c] = 1.0;
+    } else {
+      og_attention_rows(g, cand[c], d, scale, q, k, v, rows, n_rows, om);
+      for (size_t e = 0; e < n; ++e) {
+        double dd = om[e] - of[e];
+        se += dd * dd;
+      }
+      sparsity[c] = 1.0 - (double)og_mask_nnz(g, cand[c]) / (L * L);
+    }
+    mse[c] = se / (double)n;
+    loss[c] = mse[c] + (penalty == 0 ? lam * (1.0 - sparsity[c]) : lam * sparsity[c]);
+    if (best < 0 || loss[c] < loss[best]) best = c;
+  }
+  *mode = loss[best] > eps ? OG_FULL : cand[best];
+  free(of);
+  free(om);
+}
+
 /* Working layout of a head: temporal heads run on token-major indices. */
 static int working_mode(int mode) { return mode == OG_TEMPORAL ? OG_TEMPORAL_PERMUTED : mode; }
 
