@@ -86,10 +86,12 @@ typedef struct {
   int64_t b, h, x; /* element strides of batch, head and token; d is contiguous */
 } svg_strides;
 
-/* Flags of svg_sparse_attention / svg_layer_forward. */
+/* Flags of svg_sparse_attention / svg_layer_forward (and svg_workspace_bytes). */
 #define SVG_FLAG_VIRTUAL_PERMUTE 1 /* temporal heads gather rows through the
                                       token-major index instead of reading
                                       explicitly permuted copies */
+#define SVG_FLAG_MODE_SEARCH 2     /* svg_workspace_bytes only: size the
+                                      workspace for svg_search_modes */
 
 int32_t svg_abi_version(void);
 const char* svg_last_error(void);
@@ -101,14 +103,16 @@ svg_status svg_tile_config(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN)
 
 /* Workspace needed by svg_layer_forward for this geometry, input dtype,
  * number of sampled rows (0 = no profiling) and flags.  Also covers
- * svg_profile_heads (which needs a subset).  Writes *bytes. */
+ * svg_profile_heads (which needs a subset).  With SVG_FLAG_MODE_SEARCH: the
+ * workspace of svg_search_modes (bf16 only).  Writes *bytes.
+ * Errors: SVG_E_INVALID (geometry, n_rows, flags), SVG_E_UNSUPPORTED. */
 svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_rows, int32_t flags,
                                size_t* bytes);
 
 /* Online profiling (rebuttal: answer on when profiling happens; abstract:
  * head types predicted online).  For every (b, h), on the n_rows sampled
- * query rows `rows` (device int32, video rows in [T, L), shared by all heads),
- * computes full, spatial and temporal attention in one sweep over all keys,
+ * query rows `rows` (device int32, ascending distinct video rows in [T, L),
+ * shared by all heads), computes full, spatial and temporal attention,
  *   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
  * and writes labels[b*H+h] = SPATIAL if rel_s <= rel_t else TEMPORAL, or FULL
  * when min(rel_s, rel_t) >= fallback_rel_mse; stats[(b*H+h)*3 + {0,1,2}] =
@@ -118,6 +122,30 @@ svg_status svg_profile_heads(const svg_geom* geom, svg_dtype dtype, const void* 
                              const void* v, svg_strides s, const int32_t* rows, int32_t n_rows,
                              float fallback_rel_mse, int32_t* labels, float* stats, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* Offline mode search of Sparse-vDiT (review, "What carries the argument":
+ * each candidate mode's output scored by its mean squared error against full
+ * attention plus a sparsity penalty; full attention kept when every sparse
+ * candidate exceeds the threshold; referee report, major comment 1: Eq. (2)
+ * has the penalty lam*(1 - S_i), Algorithm 1 has lam*S_i, both offered).
+ * For every (b, h), on the sampled query rows (as for svg_profile_heads)
+ * computes full, WINDOW, TEMPORAL-band and STRIPE attention and scores the
+ * candidates skip (O = 0), window, temporal, stripe:
+ *   mse_c = mean over rows x d of (O_c - O_full)^2,  S_c = 1 - nnz_c / L^2
+ *   loss_c = mse_c + lam * (1 - S_c)   (penalty 0)  or  mse_c + lam * S_c  (penalty 1)
+ * (nnz_c: active pairs of the mode over the whole map, text dense; S = 1 for
+ * skip).  modes_out[b*H+h] (device int32) = the candidate with the lowest
+ * loss, ties to the earlier in that order, or FULL when every loss > eps.
+ * stats_out (device float[B*H*8]): mse_c at +0..3, loss_c at +4..7.
+ * Reductions are deterministic.  bf16 inputs only; ws: at least
+ * svg_workspace_bytes(geom, SVG_BF16, n_rows, SVG_FLAG_MODE_SEARCH) bytes,
+ * 256-byte aligned.  The resulting modes feed svg_layer_forward's modes_in.
+ * Errors: SVG_E_INVALID (arguments, lam < 0, non-finite lam/eps, penalty not
+ * 0/1), SVG_E_UNSUPPORTED (fp32), SVG_E_WORKSPACE, SVG_E_HIP. */
+svg_status svg_search_modes(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k,
+                            const void* v, svg_strides s, const int32_t* rows, int32_t n_rows, float lam,
+                            float eps, int32_t penalty, int32_t* modes_out, float* stats_out, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Key-tile lists (rebuttal Weakness 1: block-banded structure; abstract:
  * layout transformation).  For each head (modes: device int32[B*H]) and each

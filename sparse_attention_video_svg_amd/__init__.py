@@ -15,15 +15,17 @@ import math
 import os
 
 __all__ = [
-    "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE",
-    "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config", "svg_workspace_bytes",
-    "svg_profile_heads", "svg_build_blocks", "svg_layout_permute", "svg_sparse_attention",
-    "svg_layer_forward", "library_path",
+    "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE", "MODE_SEARCH",
+    "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
+    "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
+    "svg_sparse_attention", "svg_layer_forward", "library_path",
 ]
 
 SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
 F32, BF16 = 0, 1
 VIRTUAL_PERMUTE = 1
+MODE_SEARCH = 2  # svg_workspace_bytes: size for svg_search_modes
+SEARCH_CANDIDATES = (SKIP, WINDOW, TEMPORAL, STRIPE)  # order of svg_search_modes' stats
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # SVG_LIBRARY may point at another build of the same library (A/B timing).
@@ -117,6 +119,8 @@ def _lib():
             "svg_workspace_bytes": ([g, i32, i32, i32, P(ctypes.c_size_t)], i32),
             "svg_profile_heads": ([g, i32, vp, vp, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp],
                                   i32),
+            "svg_search_modes": ([g, i32, vp, vp, vp, S, vp, i32, ctypes.c_float, ctypes.c_float, i32, vp, vp, vp,
+                                  ctypes.c_size_t, vp], i32),
             "svg_build_blocks": ([g, vp, i32, i32, vp, vp, vp], i32),
             "svg_layout_permute": ([g, i32, vp, S, vp, S, vp, i32, vp], i32),
             "svg_sparse_attention": ([g, i32, i32, vp, vp, vp, S, vp, vp, vp, S, vp, S, vp, S, vp, vp, vp, i32, i32,
@@ -203,6 +207,19 @@ def svg_profile_heads(geom, q, k, v, rows, labels, stats, ws, fallback_rel_mse=0
     _check(_lib().svg_profile_heads(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _strides(q),
                                     _ptr(rows), rows.numel(), float(fallback_rel_mse), _ptr(labels), _ptr(stats),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def svg_search_modes(geom, q, k, v, rows, modes_out, stats_out, ws, lam=0.5, eps=1.0, penalty=0, stream=None):
+    """Sparse-vDiT offline mode search: modes_out int32[B*H], stats_out
+    float[B*H*8] (mse then loss of skip, window, temporal, stripe)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    g = geom.c()
+    _check(_lib().svg_search_modes(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _strides(q),
+                                   _ptr(rows), rows.numel(), float(lam), float(eps), int(penalty), _ptr(modes_out),
+                                   _ptr(stats_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def svg_build_blocks(geom, modes, BM, BN, ranges, head_order, stream=None):

@@ -116,12 +116,13 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
   size_t off = 0;
   w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows) : 0;
   const size_t rows_bh = (size_t)BH * n_rows;
+  const size_t nstates = (flags & SVG_FLAG_MODE_SEARCH) ? 4 : 3;  // masks swept per row
   w.part_acc = off;
-  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 3 * g.d);
+  off = align256(off + sizeof(float) * rows_bh * w.ksplit * nstates * g.d);
   w.part_ml = off;
-  off = align256(off + sizeof(float) * rows_bh * w.ksplit * 3 * 2);
+  off = align256(off + sizeof(float) * rows_bh * w.ksplit * nstates * 2);
   w.row_sums = off;
-  off = align256(off + sizeof(double) * rows_bh * 3);
+  off = align256(off + sizeof(double) * rows_bh * nstates);
   w.ord_x = off;
   off = align256(off + sizeof(int32_t) * (size_t)n_rows);
   w.ord_r = off;
@@ -230,13 +231,46 @@ hipError_t run_profile(const KGeom& g, svg_dtype dtype, const void* q, const voi
     int32_t* orr = ws_at<int32_t>(ws, w.ord_r);
     e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
     if (e != hipSuccess) return e;
-    e = launch_profile_bf16(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, pa, pm, st);
+    static const int32_t masks[3] = {SVG_SPATIAL, SVG_FULL, SVG_TEMPORAL};  // states 0, 1 (reference), 2
+    e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, masks, 3, pa, pm, st);
   } else {
     e = launch_profile_f32(g, q, k, v, s, rows, n_rows, pa, pm, st);
   }
   if (e != hipSuccess) return e;
   return launch_profile_merge(g, n_rows, w.ksplit, pa, pm, ws_at<double>(ws, w.row_sums), fallback, labels, stats,
                               st);
+}
+
+// Active (query, key) pairs of a mode over the whole L x L map, from the
+// closed forms of its masks: text rows and keys dense, video part per mode.
+int64_t mode_nnz(const KGeom& g, int32_t mode) {
+  if (mode == SVG_SKIP) return 0;
+  const int64_t NF = (int64_t)g.N * g.F, Lt = g.T + NF;
+  const int64_t text = Lt * Lt - NF * NF;
+  int64_t video = 0;
+  switch (mode) {
+    case SVG_SPATIAL: {
+      const int64_t a = g.a1 < g.N ? g.a1 : g.N;
+      video = (int64_t)g.F * g.F * (g.N * (2 * a - 1) - a * (a - 1));
+      break;
+    }
+    case SVG_TEMPORAL: {
+      const int64_t a = g.a2 < g.F ? g.a2 : g.F;
+      video = (int64_t)g.N * g.N * (g.F * (2 * a - 1) - a * (a - 1));
+      break;
+    }
+    case SVG_WINDOW: {
+      const int64_t w = g.window < NF ? g.window : NF;
+      video = NF * (2 * w - 1) - w * (w - 1);
+      break;
+    }
+    case SVG_STRIPE:
+      video = NF * (g.stripe < NF ? g.stripe : NF);
+      break;
+    default:
+      video = NF * NF;
+  }
+  return text + video;
 }
 
 }  // namespace
@@ -260,9 +294,47 @@ svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_
   if (!bytes) return fail(SVG_E_INVALID, "bytes is NULL");
   if (n_rows < 0 || (int64_t)n_rows > (int64_t)g.N * g.F)
     return fail(SVG_E_INVALID, "n_rows=%d must be in [0, N*F]", n_rows);
-  if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH))
+    return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & SVG_FLAG_MODE_SEARCH) && dtype != SVG_BF16)
+    return fail(SVG_E_UNSUPPORTED, "the mode search takes bf16 inputs");
   *bytes = ws_layout(g, dtype, n_rows, flags).total;
   return SVG_OK;
+}
+
+svg_status svg_search_modes(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k, const void* v,
+                            svg_strides s, const int32_t* rows, int32_t n_rows, float lam, float eps,
+                            int32_t penalty, int32_t* modes_out, float* stats_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (dtype == SVG_F32) return fail(SVG_E_UNSUPPORTED, "the mode search takes bf16 inputs");
+  TRY(validate_profile(g, dtype, q, k, v, s, rows, n_rows, 1.f, modes_out, stats_out));
+  if (!isfinite(lam) || lam < 0.f) return fail(SVG_E_INVALID, "lambda must be finite and >= 0");
+  if (!isfinite(eps)) return fail(SVG_E_INVALID, "epsilon must be finite");
+  if (penalty != 0 && penalty != 1) return fail(SVG_E_INVALID, "penalty must be 0 (lam*(1-S)) or 1 (lam*S)");
+  const WsLayout w = ws_layout(g, dtype, n_rows, SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH);
+  TRY(check_ptr(ws, "ws", 256));
+  if (ws_bytes < profile_ws_bytes(w))
+    return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, profile_ws_bytes(w));
+  SearchParams p;
+  p.lam = lam;
+  p.eps = eps;
+  p.penalty = penalty;
+  const double L2 = (double)g.L * (double)g.L;
+  const int32_t cand[4] = {SVG_SKIP, SVG_WINDOW, SVG_TEMPORAL, SVG_STRIPE};
+  for (int c = 0; c < 4; ++c) p.sparsity[c] = (float)(1.0 - (double)mode_nnz(g, cand[c]) / L2);
+  hipStream_t st = (hipStream_t)stream;
+  float* pa = ws_at<float>(ws, w.part_acc);
+  float* pm = ws_at<float>(ws, w.part_ml);
+  int32_t* ox = ws_at<int32_t>(ws, w.ord_x);
+  int32_t* orr = ws_at<int32_t>(ws, w.ord_r);
+  static const int32_t masks[4] = {SVG_FULL, SVG_WINDOW, SVG_TEMPORAL, SVG_STRIPE};  // state 0 = reference
+  hipError_t e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
+  if (e == hipSuccess) e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, masks, 4, pa, pm, st);
+  if (e == hipSuccess)
+    e = launch_search_merge(g, n_rows, w.ksplit, pa, pm, ws_at<double>(ws, w.row_sums), p, modes_out, stats_out, st);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_search_modes");
 }
 
 svg_status svg_profile_heads(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k, const void* v,

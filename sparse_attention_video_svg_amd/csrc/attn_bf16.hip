@@ -507,32 +507,28 @@ __device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, fl
 }
 
 // ---------------------------------------------------------------------------
-// Profiling sweeps: the full, spatial and temporal attention of the sampled
-// rows, each a single online-softmax state swept by the same machinery as the
-// attention kernel (8 waves x 32 rows, K/V ring in LDS).
-//   PROF_FULL      every key; the key tiles are cut into `ksplit` slices so
-//                  that the grid fills the chip, the merge combines them.
-//   PROF_SPATIAL   the row's frame run and the text prefix (frame-major keys);
-//                  the rows are ascending, so a workgroup's runs are close
-//                  and it loads only their union.
-//   PROF_TEMPORAL  the row's position band and the text prefix, with keys
-//                  gathered in token-major order through the index map and
-//                  the rows taken in position order (k_prof_rank), so again a
-//                  workgroup loads only the union of its bands.
-// Waves skip the tiles none of their rows needs.  Workgroup ids are remapped
-// so that the chunks of rows sharing one key slice of one head run together
-// on one XCD and share those K/V tiles in its L2.
-enum : int { PROF_FULL = 0, PROF_SPATIAL = 1, PROF_TEMPORAL = 2 };
-
-template <int D, int KIND, int WAVES, int STAGES>
+// Sampled-row sweeps (profiling and mode search): the attention of the
+// sampled rows under one mask, a single online-softmax state swept by the
+// same machinery as the attention kernel (8 waves x 32 rows, K/V ring in
+// LDS).  Each row's keys are one run [lo, hi) (its working-layout interval of
+// the mode) plus the text prefix; the rows of a workgroup are taken in an
+// order that keeps their runs close (ascending token for the frame-major
+// modes, ascending position for the temporal band), so a workgroup loads only
+// the union of their runs, cut into `nsplit` slices of tiles so that the grid
+// fills the chip; the merge combines the slices.  VIRT: the temporal band,
+// with keys gathered in token-major order through the index map.  Waves skip
+// the tiles none of their rows needs.  Workgroup ids are remapped so that the
+// chunks of rows sharing one slice of one head run together on one XCD and
+// share those K/V tiles in its L2.  The partial state of (row, slice) goes to
+// slot ((bh * n_rows + row) * nsplit + slice) * nstates + state.
+template <int D, bool VIRT, int WAVES, int STAGES>
 __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep(
     KGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     svg_strides s, const int32_t* __restrict__ rows, const int32_t* __restrict__ ord_r, int32_t n_rows,
-    int32_t nsplit, int32_t total, float* __restrict__ part_acc, float* __restrict__ part_ml) {
+    int32_t nsplit, int32_t total, int32_t mode, int32_t state, int32_t nstates, float* __restrict__ part_acc,
+    float* __restrict__ part_ml) {
   using C = TileCfg<D, WAVES>;
-  constexpr bool VIRT = KIND == PROF_TEMPORAL;
   constexpr int BMW = 32 * WAVES;
-  constexpr int KIND_STATE = KIND == PROF_SPATIAL ? 0 : (KIND == PROF_FULL ? 1 : 2);
   extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
   auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
   __shared__ int wb[2][WAVES];
@@ -552,61 +548,52 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
   const int rk = chunk * BMW + wave * 32 + (lane & 31);
   const bool valid = rk < n_rows;
   const int x = rows[valid ? rk : n_rows - 1];
-  const int u = x - g.T;
-  const int fi = fastdiv(u, g.divF_mul, g.divF_shift), j = u - fi * g.F;
   int lo, hi;
-  int4 rg;
-  if (KIND == PROF_FULL) {
-    lo = 0;
-    hi = g.L;
-    const int nKT = (g.L + kBN - 1) / kBN;
-    rg = make_int4((int)((int64_t)nKT * split / nsplit), (int)((int64_t)nKT * (split + 1) / nsplit), 0, 0);
+  if (VIRT) {  // the row's band in token-major order: x = T + i*F + j -> T + j*N + i
+    const int u = x - g.T;
+    const int i = fastdiv(u, g.divF_mul, g.divF_shift), j = u - i * g.F;
+    row_interval(g, SVG_TEMPORAL, x < g.T ? x : g.T + j * g.N + i, lo, hi);
   } else {
-    if (KIND == PROF_SPATIAL) {
-      lo = g.T + max(0, fi - g.a1 + 1) * g.F;
-      hi = g.T + min(g.N, fi + g.a1) * g.F;
-    } else {
-      lo = g.T + max(0, j - g.a2 + 1) * g.N;
-      hi = g.T + min(g.F, j + g.a2) * g.N;
-    }
-    // the workgroup's union of runs -> tile ranges (text tiles first)
-    const int wlo = wave_min_i(valid ? lo : INT_MAX), whi = wave_max_i(valid ? hi : INT_MIN);
-    if (lane == 0) {
-      wb[0][wave] = wlo;
-      wb[1][wave] = whi;
-    }
-    __syncthreads();
-    int ulo = wb[0][0], uhi = wb[1][0];
-#pragma unroll
-    for (int i = 1; i < WAVES; ++i) {
-      ulo = min(ulo, wb[0][i]);
-      uhi = max(uhi, wb[1][i]);
-    }
-    const int bs = ulo / kBN, be = (uhi + kBN - 1) / kBN, te = (g.T + kBN - 1) / kBN;
-    int4 u4;
-    if (g.T == 0)
-      u4 = make_int4(bs, be, 0, 0);
-    else if (te >= bs)
-      u4 = make_int4(0, max(be, te), 0, 0);
-    else
-      u4 = make_int4(0, te, bs, be);
-    // this workgroup's slice of the concatenated tile sequence
-    const int n1 = u4.y - u4.x, nt = n1 + (u4.w - u4.z);
-    const int t0 = (int)((int64_t)nt * split / nsplit), t1 = (int)((int64_t)nt * (split + 1) / nsplit);
-    rg.x = u4.x + min(t0, n1);
-    rg.y = u4.x + min(t1, n1);
-    rg.z = u4.z + max(t0 - n1, 0);
-    rg.w = u4.z + max(t1 - n1, 0);
+    row_interval(g, mode, x, lo, hi);
   }
+  // the workgroup's union of runs -> tile ranges (text tiles first)
+  const int wlo = wave_min_i(valid ? lo : INT_MAX), whi = wave_max_i(valid ? hi : INT_MIN);
+  if (lane == 0) {
+    wb[0][wave] = wlo;
+    wb[1][wave] = whi;
+  }
+  __syncthreads();
+  int ulo = wb[0][0], uhi = wb[1][0];
+#pragma unroll
+  for (int i = 1; i < WAVES; ++i) {
+    ulo = min(ulo, wb[0][i]);
+    uhi = max(uhi, wb[1][i]);
+  }
+  const int bs = ulo / kBN, be = (uhi + kBN - 1) / kBN, te = (g.T + kBN - 1) / kBN;
+  int4 u4;
+  if (g.T == 0)
+    u4 = make_int4(bs, be, 0, 0);
+  else if (te >= bs)
+    u4 = make_int4(0, max(be, te), 0, 0);
+  else
+    u4 = make_int4(0, te, bs, be);
+  // this workgroup's slice of the concatenated tile sequence
+  const int n1 = u4.y - u4.x, nt = n1 + (u4.w - u4.z);
+  const int t0 = (int)((int64_t)nt * split / nsplit), t1 = (int)((int64_t)nt * (split + 1) / nsplit);
+  int4 rg;
+  rg.x = u4.x + min(t0, n1);
+  rg.y = u4.x + min(t1, n1);
+  rg.z = u4.z + max(t0 - n1, 0);
+  rg.w = u4.z + max(t1 - n1, 0);
+
   bf16x8 qf[D / 16];
   load_q<D>(qf, q + base + (int64_t)x * s.x, hh);
   Flash<D> st;
   run_sweep<D, VIRT, WAVES, STAGES>(st, qf, k + base, v + base, s.x, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
-    // slot (row, slice, state): state 0 spatial, 1 full, 2 temporal; the
-    // temporal sweep's rows come in position order, ord_r maps them back
-    const int r = KIND == PROF_TEMPORAL ? ord_r[rk] : rk;
-    const int64_t o = (((int64_t)bh * n_rows + r) * nsplit + split) * 3 + KIND_STATE;
+    // temporal rows come in position order; ord_r maps them back
+    const int r = VIRT ? ord_r[rk] : rk;
+    const int64_t o = (((int64_t)bh * n_rows + r) * nsplit + split) * nstates + state;
     store_partial<D>(st, part_acc + o * D, part_ml + o * 2, hh);
   }
 }
@@ -638,13 +625,13 @@ hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf1
   return out_bf16 ? launch_attn<128, true>(g, a, nQT, grid, total, st) : launch_attn<128, false>(g, a, nQT, grid, total, st);
 }
 
-template <int D, int KIND>
+template <int D, bool VIRT>
 static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
-                              const int32_t* rows, const int32_t* ord_r, int32_t n_rows, int32_t nsplit,
-                              float* acc, float* ml, hipStream_t st) {
+                              const int32_t* rows, const int32_t* ord_r, int32_t n_rows, int32_t nsplit, int32_t mode,
+                              int32_t state, int32_t nstates, float* acc, float* ml, hipStream_t st) {
   constexpr int W = kAttnWaves, S = kAttnStages;
   const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
-  auto kern = k_prof_sweep<D, KIND, W, S>;
+  auto kern = k_prof_sweep<D, VIRT, W, S>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -657,28 +644,35 @@ static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, 
   const int64_t grid = (total + per_round - 1) / per_round * per_round;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, q, k, v, s, rows, ord_r, n_rows, nsplit,
-                     (int32_t)total, acc, ml);
+                     (int32_t)total, mode, state, nstates, acc, ml);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_prof_all(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
-                                  const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
-                                  const int32_t* ord_r, float* acc, float* ml, hipStream_t st) {
-  hipError_t e = launch_prof<D, PROF_FULL>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, acc, ml, st);
-  if (e != hipSuccess) return e;
-  e = launch_prof<D, PROF_SPATIAL>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, acc, ml, st);
-  if (e != hipSuccess) return e;
-  return launch_prof<D, PROF_TEMPORAL>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, acc, ml, st);
+static hipError_t launch_sweeps(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
+                                const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                                const int32_t* ord_r, const int32_t* modes, int32_t nstates, float* acc, float* ml,
+                                hipStream_t st) {
+  for (int32_t i = 0; i < nstates; ++i) {
+    hipError_t e;
+    if (modes[i] == SVG_TEMPORAL)
+      e = launch_prof<D, true>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, SVG_TEMPORAL, i, nstates, acc, ml, st);
+    else
+      e = launch_prof<D, false>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates, acc, ml, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                               const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
-                               const int32_t* ord_r, float* acc, float* ml, hipStream_t st) {
+hipError_t launch_sample_sweeps(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
+                                const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                                const int32_t* ord_r, const int32_t* modes, int32_t nstates, float* acc, float* ml,
+                                hipStream_t st) {
   const __bf16 *bq = static_cast<const __bf16*>(q), *bk = static_cast<const __bf16*>(k),
                *bv = static_cast<const __bf16*>(v);
-  if (g.d == 64) return launch_prof_all<64>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, acc, ml, st);
-  return launch_prof_all<128>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, acc, ml, st);
+  if (g.d == 64)
+    return launch_sweeps<64>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, modes, nstates, acc, ml, st);
+  return launch_sweeps<128>(g, bq, bk, bv, s, rows, n_rows, ksplit, ord_x, ord_r, modes, nstates, acc, ml, st);
 }
 
 }  // namespace svg

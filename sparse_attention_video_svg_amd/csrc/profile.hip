@@ -6,10 +6,15 @@
 // and the temporal mask on the sampled rows:
 //   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
 //   label = SPATIAL if rel_s <= rel_t else TEMPORAL, FULL if min >= fallback.
-// The sweeps leave per row and key slice three partial states (m in log2
-// units, l, unnormalised acc): spatial, full and temporal.  Rows are merged in
-// parallel, each row's three squared-error sums are written, and one
-// workgroup per head adds them in a fixed order.
+// The mode search (Sparse-vDiT review: offline search scoring each candidate
+// mode by its MSE against full attention plus a sparsity penalty, full
+// attention kept when every candidate exceeds the threshold) reuses the same
+// sweeps with the window, temporal-band and stripe masks.
+// The sweeps leave per row and key slice one partial state per mask (m in
+// log2 units, l, unnormalised acc): for profiling spatial, full and temporal,
+// for the mode search full, window, temporal band and stripe.  Rows are merged
+// in parallel, each row's squared-error sums are written, and one workgroup
+// per head adds them in a fixed order.
 #include "svg_device.h"
 
 namespace svg {
@@ -49,23 +54,29 @@ __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n
 }
 
 // One workgroup (D threads, one per dim) per (sampled row, head): each of
-// the three states merged over the key slices, then normalised.
+// the nstates states merged over the key slices and normalised, then the
+// row's sums over d: sum O_ref^2 at index ref, sum (O_s - O_ref)^2 at every
+// other index s.
+constexpr int kMaxStates = 4;
+
 template <int D>
-__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit,
+__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit, int32_t nstates, int32_t ref,
                                                        const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        double* __restrict__ row_sums) {
   const int r = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
   const int64_t row = (int64_t)bh * n_rows + r;
-  float o[3];
+  float o[kMaxStates];
 #pragma unroll
-  for (int st = 0; st < 3; ++st) {
+  for (int st = 0; st < kMaxStates; ++st) {
+    o[st] = 0.f;
+    if (st >= nstates) continue;
     float m = -INFINITY;
-    for (int s = 0; s < ksplit; ++s) m = fmaxf(m, part_ml[((row * ksplit + s) * 3 + st) * 2]);
+    for (int s = 0; s < ksplit; ++s) m = fmaxf(m, part_ml[((row * ksplit + s) * nstates + st) * 2]);
     float l = 0.f, a = 0.f;
     if (m != -INFINITY) {
       for (int s = 0; s < ksplit; ++s) {
-        const int64_t slot = (row * ksplit + s) * 3 + st;
+        const int64_t slot = (row * ksplit + s) * nstates + st;
         const float w = exp2f(part_ml[slot * 2] - m);
         l += w * part_ml[slot * 2 + 1];
         a += w * part_acc[slot * D + c];
@@ -73,51 +84,97 @@ __global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t k
     }
     o[st] = l > 0.f ? a / l : 0.f;
   }
-  const float o_sp = o[0], o_f = o[1], o_tp = o[2];
-  const double ds = (double)o_sp - (double)o_f, dt = (double)o_tp - (double)o_f;
-  __shared__ double red[3][D];
-  red[0][c] = ds * ds;
-  red[1][c] = dt * dt;
-  red[2][c] = (double)o_f * (double)o_f;
+  float o_ref = o[0];
+#pragma unroll
+  for (int st = 1; st < kMaxStates; ++st) o_ref = st == ref ? o[st] : o_ref;
+  __shared__ double red[kMaxStates][D];
+#pragma unroll
+  for (int st = 0; st < kMaxStates; ++st) {
+    const double dd = st == ref ? (double)o_ref : (double)o[st] - (double)o_ref;
+    red[st][c] = dd * dd;
+  }
   __syncthreads();
   for (int w = D / 2; w > 0; w >>= 1) {
     if (c < w) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) red[k][c] += red[k][c + w];
+      for (int k = 0; k < kMaxStates; ++k) red[k][c] += red[k][c + w];
     }
     __syncthreads();
   }
-  if (c < 3) row_sums[row * 3 + c] = red[c][0];
+  if (c < nstates) row_sums[row * nstates + c] = red[c][0];
 }
 
-__global__ __launch_bounds__(256) void k_prof_finalize(int32_t d, int32_t n_rows, const double* __restrict__ row_sums,
-                                                       float fallback, int32_t* __restrict__ labels,
-                                                       float* __restrict__ stats) {
-  const int bh = blockIdx.x, t = threadIdx.x;
-  double acc[3] = {0.0, 0.0, 0.0};
+// Per-head fixed-order sums of the row sums (one workgroup per head).
+template <int NS>
+__device__ __forceinline__ void head_sums(int bh, int n_rows, const double* __restrict__ row_sums, double* out) {
+  const int t = threadIdx.x;
+  double acc[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) acc[k] = 0.0;
   for (int r = t; r < n_rows; r += 256)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) acc[k] += row_sums[((int64_t)bh * n_rows + r) * 3 + k];
-  __shared__ double red[3][256];
+    for (int k = 0; k < NS; ++k) acc[k] += row_sums[((int64_t)bh * n_rows + r) * NS + k];
+  __shared__ double red[NS][256];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) red[k][t] = acc[k];
+  for (int k = 0; k < NS; ++k) red[k][t] = acc[k];
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (t < w) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) red[k][t] += red[k][t + w];
+      for (int k = 0; k < NS; ++k) red[k][t] += red[k][t + w];
     }
     __syncthreads();
   }
-  if (t == 0) {
-    const double den = red[2][0];
-    const double rs = den > 0.0 ? red[0][0] / den : INFINITY;
-    const double rt = den > 0.0 ? red[1][0] / den : INFINITY;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) out[k] = red[k][0];
+}
+
+// Profiling labels: states 0 spatial, 1 full (reference), 2 temporal.
+__global__ __launch_bounds__(256) void k_prof_finalize(int32_t d, int32_t n_rows, const double* __restrict__ row_sums,
+                                                       float fallback, int32_t* __restrict__ labels,
+                                                       float* __restrict__ stats) {
+  const int bh = blockIdx.x;
+  double sum[3];
+  head_sums<3>(bh, n_rows, row_sums, sum);
+  if (threadIdx.x == 0) {
+    const double den = sum[1];
+    const double rs = den > 0.0 ? sum[0] / den : INFINITY;
+    const double rt = den > 0.0 ? sum[2] / den : INFINITY;
     const double best = rs <= rt ? rs : rt;
     labels[bh] = best >= (double)fallback ? SVG_FULL : (rs <= rt ? SVG_SPATIAL : SVG_TEMPORAL);
     stats[bh * 3 + 0] = (float)rs;
     stats[bh * 3 + 1] = (float)rt;
     stats[bh * 3 + 2] = (float)(den / ((double)n_rows * d));
+  }
+}
+
+// Mode search: states 0 full (reference), 1 window, 2 temporal band, 3
+// stripe; the skip candidate's error is the reference's own sum of squares.
+// Candidates in the order skip, window, temporal, stripe (ties to the
+// earlier); loss = mse + lam * (1 - S) or mse + lam * S; FULL when every
+// loss exceeds eps.  stats[bh * 8]: mse[4] then loss[4].
+__global__ __launch_bounds__(256) void k_search_finalize(int32_t d, int32_t n_rows, const double* __restrict__ row_sums,
+                                                         SearchParams p, int32_t* __restrict__ modes,
+                                                         float* __restrict__ stats) {
+  const int bh = blockIdx.x;
+  double sum[4];
+  head_sums<4>(bh, n_rows, row_sums, sum);
+  if (threadIdx.x == 0) {
+    const double n = (double)n_rows * d;
+    const int cand[4] = {SVG_SKIP, SVG_WINDOW, SVG_TEMPORAL, SVG_STRIPE};
+    const double se[4] = {sum[0], sum[1], sum[2], sum[3]};
+    int best = 0;
+    double loss[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double mse = se[c] / n;
+      const double sp = (double)p.sparsity[c];
+      loss[c] = mse + (p.penalty == 0 ? (double)p.lam * (1.0 - sp) : (double)p.lam * sp);
+      if (loss[c] < loss[best]) best = c;
+      stats[bh * 8 + c] = (float)mse;
+      stats[bh * 8 + 4 + c] = (float)loss[c];
+    }
+    modes[bh] = loss[best] > (double)p.eps ? SVG_FULL : cand[best];
   }
 }
 
@@ -128,16 +185,36 @@ hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_ro
   return hipGetLastError();
 }
 
+hipError_t launch_prof_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t nstates, int32_t ref,
+                             const float* part_acc, const float* part_ml, double* row_sums, hipStream_t st) {
+  if (nstates < 1 || nstates > kMaxStates) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
+  if (g.d == 64)
+    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, nstates, ref, part_acc, part_ml,
+                       row_sums);
+  else
+    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, nstates, ref, part_acc,
+                       part_ml, row_sums);
+  return hipGetLastError();
+}
+
 hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
                                 const float* part_ml, double* row_sums, float fallback, int32_t* labels, float* stats,
                                 hipStream_t st) {
-  dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
-  if (g.d == 64)
-    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, part_acc, part_ml, row_sums);
-  else
-    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, part_acc, part_ml, row_sums);
+  hipError_t e = launch_prof_merge(g, n_rows, ksplit, 3, 1, part_acc, part_ml, row_sums, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_prof_finalize, dim3((unsigned)(g.B * g.H)), dim3(256), 0, st, g.d, n_rows, row_sums, fallback,
                      labels, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_search_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
+                               const float* part_ml, double* row_sums, const SearchParams& p, int32_t* modes,
+                               float* stats, hipStream_t st) {
+  hipError_t e = launch_prof_merge(g, n_rows, ksplit, 4, 0, part_acc, part_ml, row_sums, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_search_finalize, dim3((unsigned)(g.B * g.H)), dim3(256), 0, st, g.d, n_rows, row_sums, p,
+                     modes, stats);
   return hipGetLastError();
 }
 

@@ -61,20 +61,33 @@ struct AttnPtrs {
 hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, int32_t BN, hipStream_t st);
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st);
 
-// Profiling: the sweeps write, per (head, row, key slice), three partial
-// online-softmax states (m in log2 units, l, unnormalised acc): 0 spatial,
-// 1 full, 2 temporal, at slot ((bh * n_rows + row) * ksplit + slice) * 3 +
-// state.  The merge reduces them, deterministically, into labels and stats.
+// Sampled-row sweeps (profiling, mode search): per (head, row, key slice)
+// one partial online-softmax state (m in log2 units, l, unnormalised acc) per
+// mask, at slot ((bh * n_rows + row) * ksplit + slice) * nstates + state.
+// Profiling: nstates 3 = spatial, full, temporal.  Mode search: nstates 4 =
+// full, window, temporal band, stripe.  The merges reduce them,
+// deterministically, into labels / modes and stats.
+struct SearchParams {
+  float lam, eps;
+  int32_t penalty;     // 0: lam * (1 - S), 1: lam * S
+  float sparsity[4];   // S of skip, window, temporal, stripe
+};
 hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
                                hipStream_t st);
 hipError_t launch_profile_f32(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
                               const int32_t* rows, int32_t n_rows, float* part_acc, float* part_ml, hipStream_t st);
-hipError_t launch_profile_bf16(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
-                               const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
-                               const int32_t* ord_r, float* part_acc, float* part_ml, hipStream_t st);
+// bf16: one sweep per entry of modes[nstates] (state i = modes[i]; TEMPORAL
+// is the band through the index map, rows in position order ord_x / ord_r).
+hipError_t launch_sample_sweeps(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
+                                const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
+                                const int32_t* ord_r, const int32_t* modes, int32_t nstates, float* part_acc,
+                                float* part_ml, hipStream_t st);
 hipError_t launch_profile_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
                                 const float* part_ml, double* row_sums, float fallback, int32_t* labels, float* stats,
                                 hipStream_t st);
+hipError_t launch_search_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, const float* part_acc,
+                               const float* part_ml, double* row_sums, const SearchParams& p, int32_t* modes,
+                               float* stats, hipStream_t st);
 
 // Tile sizes of the bf16 MFMA attention kernel (32 query rows per wave, a
 // ring of kAttnStages K/V tiles of 64 keys in LDS) and of the fp32 kernel.

@@ -169,3 +169,35 @@ def test_blocks_permute_layer_validation():
                                1 << 40, None) == E_INVALID
     assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, None, A, 0,
                                A, 1 << 40, None) == E_INVALID
+
+
+def test_search_validation():
+    g = geom().c()
+    L = raw()
+    s = strides()
+    base = dict(dt=svg.BF16, rows=A, n=8, lam=0.5, eps=1.0, pen=0, modes=A, stats=A, ws=A, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.svg_search_modes(ctypes.byref(g), a["dt"], A, A, A, s, a["rows"], a["n"], a["lam"], a["eps"],
+                                  a["pen"], a["modes"], a["stats"], a["ws"], a["wsb"], None)
+
+    assert call(dt=svg.F32) == E_UNSUPPORTED
+    assert call(rows=None) == E_INVALID
+    assert call(n=0) == E_INVALID
+    assert call(lam=-0.1) == E_INVALID
+    assert call(lam=float("inf")) == E_INVALID
+    assert call(eps=float("nan")) == E_INVALID
+    assert call(pen=2) == E_INVALID
+    assert call(modes=None) == E_INVALID
+    assert call(stats=None) == E_INVALID
+    assert call(ws=A + 16) == E_INVALID
+    assert call(wsb=16) == E_WORKSPACE
+    gg = geom()
+    plain = svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.VIRTUAL_PERMUTE)
+    search = svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.MODE_SEARCH | svg.VIRTUAL_PERMUTE)
+    assert search > plain
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_workspace_bytes(gg, svg.F32, 16, svg.MODE_SEARCH)
+    assert e.value.status == E_UNSUPPORTED

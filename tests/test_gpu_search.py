@@ -1,0 +1,99 @@
+"""GPU parity of svg_search_modes, the Sparse-vDiT offline mode search
+(candidates skip / window / temporal band / stripe scored by MSE against full
+attention plus a sparsity penalty, FULL when every loss exceeds eps), against
+the oracle's og_search_head on the same sampled rows (marked gpu).
+
+Bars: per-head MSE and loss within rtol 2e-2 (absolute floor 1e-5: near-zero
+errors of the planted mode are bf16-rounding noise); the chosen mode equal to
+the oracle's wherever the oracle's best loss is separated by more than that
+tolerance from the runner-up and from eps, and a valid candidate otherwise."""
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_video_svg_amd as svg
+import svg_synth as S
+from helpers import ogeom, scale_of, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+KINDS5 = [S.FULL, S.SKIP, S.WINDOW, S.TEMPORAL, S.STRIPE]
+RTOL, ATOL = 2e-2, 1e-5
+
+
+def run_search(g, inp, rows_np, lam, eps, penalty):
+    BH = g.B * g.H
+    q, k, v = (to_device(inp[n].reshape(g.B, g.H, g.L, g.d), torch.bfloat16) for n in "qkv")
+    rows = torch.from_numpy(rows_np.astype(np.int32)).cuda()
+    ws = svg.alloc_workspace(g, svg.BF16, rows.numel(), svg.MODE_SEARCH)
+    modes = torch.full((BH,), -1, dtype=torch.int32, device="cuda")
+    stats = torch.full((BH * 8,), float("nan"), dtype=torch.float32, device="cuda")
+    svg.svg_search_modes(g, q, k, v, rows, modes, stats, ws, lam=lam, eps=eps, penalty=penalty)
+    torch.cuda.synchronize()
+    return modes.cpu().numpy(), stats.cpu().numpy().reshape(BH, 8)
+
+
+def check_heads(g, inp, rows_np, heads, lam, eps, penalty, modes, stats):
+    og = ogeom(g)
+    for h in heads:
+        want, mse, loss, _ = oracle.search_head(og, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows_np,
+                                                lam=lam, eps=eps, penalty=penalty)
+        np.testing.assert_allclose(stats[h, :4], mse, rtol=RTOL, atol=ATOL, err_msg=f"mse head {h}")
+        np.testing.assert_allclose(stats[h, 4:], loss, rtol=RTOL, atol=ATOL, err_msg=f"loss head {h}")
+        lo = np.sort(loss)
+        tol = RTOL * abs(lo[0]) + 2 * ATOL
+        if lo[1] - lo[0] > tol and abs(lo[0] - eps) > tol:
+            assert modes[h] == want, (h, modes[h], want, loss, stats[h])
+        else:
+            assert modes[h] in (svg.FULL,) + svg.SEARCH_CANDIDATES
+
+
+@pytest.mark.parametrize("B,N,F,T,d,stripe,lam,penalty", [
+    (1, 6, 48, 0, 64, 32, 0.5, 0), (1, 6, 48, 0, 64, 32, 0.5, 1), (1, 6, 48, 0, 64, 32, 1e-4, 0),
+    (1, 5, 60, 9, 128, 40, 1e-4, 1), (2, 7, 40, 0, 128, 64, 0.5, 0), (1, 9, 37, 3, 128, 20, 0.05, 0)])
+def test_search_small_shapes(B, N, F, T, d, stripe, lam, penalty):
+    H = len(KINDS5)
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T, a1=2, a2=8, window=F, stripe=stripe)
+    inp = S.small_config(N, F, T, B * H, d, 2, 8, KINDS5 * B, seed=11 * N + d, window=F, stripe=stripe)
+    rows_np = S.sample_rows(N, F, T, 0.2, N + F)
+    print(f"\n[search B={B} N={N} F={F} T={T} d={d} lam={lam} penalty={penalty}]", flush=True)
+    modes, stats = run_search(g, inp, rows_np, lam, 1.0, penalty)
+    check_heads(g, inp, rows_np, range(B * H), lam, 1.0, penalty, modes, stats)
+
+
+def test_search_fallback_and_determinism():
+    """eps below every loss: all heads FULL; a rerun gives identical bits."""
+    H = len(KINDS5)
+    N, F, d = 6, 48, 64
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=0, a1=2, a2=8, window=F, stripe=32)
+    inp = S.small_config(N, F, 0, H, d, 2, 8, KINDS5, seed=3, window=F, stripe=32)
+    rows_np = S.sample_rows(N, F, 0, 0.2, 1)
+    modes, stats = run_search(g, inp, rows_np, 0.5, -1.0, 0)
+    assert np.all(modes == svg.FULL)
+    modes2, stats2 = run_search(g, inp, rows_np, 0.5, -1.0, 0)
+    assert np.array_equal(stats.view(np.uint32), stats2.view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("lam", [1e-4, 0.5])
+def test_search_sparse_vdit_shape(lam):
+    """The Sparse-vDiT pattern-set shape (21 x 1560 tokens, 40 heads, d 128,
+    8 heads per planted kind), 1 % of the video rows sampled; the oracle
+    checks 2 heads of each kind, the planted window / temporal / stripe heads
+    must pick their own mode when the penalty is small."""
+    c = S.CONFIGS[4]
+    inp = S.make_inputs(4, call=0)
+    g = svg.Geom(B=1, H=c["H"], d=c["d"], N=c["N"], F=c["F"], T=c["T"], a1=c["a1"], a2=c["a2"],
+                 window=c["window"], stripe=c["stripe"])
+    rows_np = S.sample_rows(c["N"], c["F"], c["T"], 0.01, 4500)
+    print(f"\n[search sparse-vdit shape lam={lam}, {rows_np.size} rows]", flush=True)
+    modes, stats = run_search(g, inp, rows_np, lam, 1.0, 0)
+    kinds = inp["kinds"]
+    heads = [h for kd in KINDS5 for h in np.flatnonzero(kinds == kd)[:2]]
+    check_heads(g, inp, rows_np, heads, lam, 1.0, 0, modes, stats)
+    if lam < 1e-3:
+        want = {S.WINDOW: svg.WINDOW, S.TEMPORAL: svg.TEMPORAL, S.STRIPE: svg.STRIPE}
+        for h, kd in enumerate(kinds):
+            if kd in want:
+                assert modes[h] == want[kd], (h, kd, modes[h], stats[h])
