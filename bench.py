@@ -13,7 +13,12 @@ give the sparse-attention kernel alone (the a5 figure), measured with HIP
 events on the stream the kernels run on.
 
   python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
-                  [--virtual] [--calib-copy]
+                  [--virtual] [--calib-copy] [--search]
+
+--search also times the Sparse-vDiT offline mode search (svg_search_modes:
+full, window, temporal-band and stripe attention of the sampled rows, 1 % of
+the video rows when the workload samples none) on the same inputs and adds
+search_* fields.
 """
 import argparse
 import json
@@ -127,6 +132,50 @@ def cpu_baseline(cfg, inp, labels, d, scale, budget_s=12.0):
                       f"{[int(labels[h]) for h in heads]}), fp64 oracle masked attention, {elapsed:.1f} s"}
 
 
+def search_keys(geom, rows):
+    """Keys per sampled row summed over the four masks the mode search sweeps
+    (full, window, temporal band, stripe), from the masks' closed forms."""
+    import numpy as np
+    N, F, T = geom.N, geom.F, geom.T
+    n = N * F
+    u = rows.astype(np.int64) - T
+    j = u % F
+    full = T + n
+    window = T + np.minimum(u + geom.window, n) - np.maximum(u - geom.window + 1, 0)
+    temporal = T + N * (np.minimum(F, j + geom.a2) - np.maximum(0, j - geom.a2 + 1))
+    stripe = T + min(geom.stripe, n)
+    return float(np.sum(full + window + temporal + stripe))
+
+
+def time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch):
+    rows_np = inp["rows"]
+    if rows_np is None:
+        rows_np = S.sample_rows(geom.N, geom.F, geom.T, 0.01, inp["seed"] + 500)
+    rows = torch.from_numpy(rows_np.astype(np.int32)).to(dev)
+    ws = svg.alloc_workspace(geom, svg.BF16, rows.numel(), svg.MODE_SEARCH | svg.VIRTUAL_PERMUTE)
+    modes = torch.empty(geom.B * geom.H, dtype=torch.int32, device=dev)
+    stats = torch.empty(geom.B * geom.H * 8, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        svg.svg_search_modes(geom, q, k, v, rows, modes, stats, ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        svg.svg_search_modes(geom, q, k, v, rows, modes, stats, ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = 4.0 * geom.d * geom.B * geom.H * search_keys(geom, rows_np)
+    m = modes.cpu().numpy()
+    names = {svg.FULL: "full", svg.SKIP: "skip", svg.WINDOW: "window", svg.TEMPORAL: "temporal",
+             svg.STRIPE: "stripe"}
+    log(f"mode search: {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    return {"search_ms": round(ms, 4), "search_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "search_rows": int(rows_np.size), "search_lambda": 0.5, "search_eps": 1.0,
+            "search_modes": {nm: int((m == c).sum()) for c, nm in names.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +187,7 @@ def main():
     ap.add_argument("--virtual", action="store_true",
                     help="temporal heads gather through the index map instead of explicit permutes")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--search", action="store_true", help="also time svg_search_modes on the same inputs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by head with no "
@@ -278,6 +328,8 @@ def main():
                      "traffic": recorded_traffic() if args.config == 2 and not args.virtual else None,
                      "kernel": "k_attn_bf16 (svg_sparse_attention)" if bf16 else "k_attn_f32"},
     }
+    if args.search and bf16:
+        result.update(time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch))
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, lab, d, 1.0 / np.sqrt(d))

@@ -30,3 +30,20 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("N,F,T", [(4, 7, 3), (5, 6, 0), (3, 20, 11)])
+def test_search_key_count_matches_oracle_intervals(oracle_lib, N, F, T):
+    """The mode search's work figure: keys per sampled row over the four masks
+    it sweeps (full, window, temporal band, stripe) equals the oracle's
+    per-row intervals summed."""
+    import sparse_attention_video_svg_amd as svg
+    for a1, a2, W, S in [(1, 2, 3, 4), (2, 9, 50, 2)]:
+        g = oracle.geom(N, F, T, a1, a2, W, S)
+        geom = svg.Geom(B=1, H=1, d=64, N=N, F=F, T=T, a1=a1, a2=a2, window=W, stripe=S)
+        rows = np.arange(T, T + N * F, 3, dtype=np.int32)
+        want = 0
+        for x in rows:
+            for mode in (oracle.FULL, oracle.WINDOW, oracle.TEMPORAL, oracle.STRIPE):
+                want += sum(h - l for l, h in oracle.row_intervals(g, mode, int(x)))
+        assert bench.search_keys(geom, rows) == want
