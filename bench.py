@@ -30,6 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# fp8 scores + bf16 P.V: half the attention FLOPs at each rate
+PEAK_FP8_QK_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -188,6 +191,8 @@ def main():
                     help="temporal heads gather through the index map instead of explicit permutes")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--search", action="store_true", help="also time svg_search_modes on the same inputs")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 E4M3 scores: quantise Q, K (svg_quantize_qk) and run svg_sparse_attention_fp8")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by head with no "
@@ -225,6 +230,15 @@ def main():
     ranges = torch.empty(H * nQT * 4, dtype=torch.int32, device=dev)
     order = torch.empty(H, dtype=torch.int32, device=dev)
     ws = svg.alloc_workspace(geom, din, n_rows, svg.VIRTUAL_PERMUTE)
+    if args.fp8:
+        if not bf16:
+            sys.exit("--fp8 needs a bf16 workload")
+        args.virtual = True  # the fp8 path reads temporal heads through the index map
+        nkt = -(-L // 64)
+        q8 = torch.empty(H * L * d, dtype=torch.uint8, device=dev)
+        k8 = torch.empty_like(q8)
+        sq = torch.empty(H * L, dtype=torch.float32, device=dev)
+        sk = torch.empty(H * nkt, dtype=torch.float32, device=dev)
     flags = svg.VIRTUAL_PERMUTE if args.virtual else 0
     if not args.virtual:
         qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
@@ -246,11 +260,17 @@ def main():
         marks.append(ev()); marks[-1].record(stream)
         svg.svg_build_blocks(geom, modes, BM, BN, ranges, order)
         marks.append(ev()); marks[-1].record(stream)
-        if not args.virtual:
+        if args.fp8:
+            svg.svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk)
+        elif not args.virtual:
             for s_, d_ in ((q, qp), (k, kp), (v, vp)):
                 svg.svg_layout_permute(geom, s_, d_, modes=modes)
         marks.append(ev()); marks[-1].record(stream)
-        svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op, flags=flags)
+        if args.fp8:
+            svg.svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, order)
+        else:
+            svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op,
+                                     flags=flags)
         marks.append(ev()); marks[-1].record(stream)
         if not args.virtual:
             svg.svg_layout_permute(geom, op, o, modes=modes, inverse=True)
@@ -289,12 +309,13 @@ def main():
     flops = 4.0 * d * float(sum(pairs))
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    peak = (PEAK_FP8_QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS) if bf16 else PEAK_F32_TFLOPS
     n_temporal = int((lab == 1).sum())
     elt = 2 if bf16 else 4
     perm_bytes = 2.0 * n_temporal * L * d * elt  # read + write per permuted head-tensor
-    fwd_gbs = 3 * perm_bytes / (perm_ms * 1e-3) / 1e9 if perm_ms > 0 and n_temporal else None
-    inv_gbs = perm_bytes / (inv_ms * 1e-3) / 1e9 if inv_ms > 0 and n_temporal else None
+    explicit = not args.virtual and n_temporal
+    fwd_gbs = 3 * perm_bytes / (perm_ms * 1e-3) / 1e9 if explicit and perm_ms > 0 else None
+    inv_gbs = perm_bytes / (inv_ms * 1e-3) / 1e9 if explicit and inv_ms > 0 else None
     result = {
         "metric": "sparse-attn ms/layer + effective TFLOP/s vs bf16 MFMA peak (33x3600x24h x d128)",
         "value": round(step_tflops, 2),
@@ -311,22 +332,25 @@ def main():
         "config": {"workload": f"{cfg['name']} (config {args.config})", "frames": geom.N,
                    "tokens_per_frame": geom.F, "text_tokens": geom.T, "heads": H, "head_dim": d,
                    "a1": geom.a1, "a2": geom.a2, "sampled_rows": n_rows, "layout": "virtual" if args.virtual
-                   else "explicit", "labels": {"spatial": int((lab == 0).sum()), "temporal": n_temporal,
+                   else "explicit", "scores": "fp8-e4m3 (Q per row, K per 64-key tile)" if args.fp8 else "bf16",
+                   "labels": {"spatial": int((lab == 0).sum()), "temporal": n_temporal,
                                                "full": int((lab == 2).sum()), "other": int((lab > 2).sum())}},
         "attn_ms": round(float(attn_ms), 4),
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_of_peak": round(attn_tflops / peak, 4),
         "profile_ms": round(float(prof_ms), 4),
         "blocks_ms": round(float(blocks_ms), 4),
-        "permute_fwd_ms": round(float(perm_ms), 4),
+        "permute_fwd_ms": None if args.fp8 else round(float(perm_ms), 4),
+        "quant_ms": round(float(perm_ms), 4) if args.fp8 else None,
         "permute_inv_ms": round(float(inv_ms), 4),
         "permute_fwd_gbs": None if fwd_gbs is None else round(fwd_gbs, 1),
         "permute_inv_gbs": None if inv_gbs is None else round(inv_gbs, 1),
         "effective_flops_per_layer": flops,
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
-                     "traffic": recorded_traffic() if args.config == 2 and not args.virtual else None,
-                     "kernel": "k_attn_bf16 (svg_sparse_attention)" if bf16 else "k_attn_f32"},
+                     "traffic": recorded_traffic() if args.config == 2 and not args.virtual and not args.fp8 else None,
+                     "kernel": ("k_attn_fp8 (svg_sparse_attention_fp8)" if args.fp8 else
+                                "k_attn_bf16 (svg_sparse_attention)") if bf16 else "k_attn_f32"},
     }
     if args.search and bf16:
         result.update(time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch))

@@ -92,6 +92,10 @@ typedef struct {
                                       explicitly permuted copies */
 #define SVG_FLAG_MODE_SEARCH 2     /* svg_workspace_bytes only: size the
                                       workspace for svg_search_modes */
+#define SVG_FLAG_FP8_SCORES 4      /* svg_layer_forward (and its workspace):
+                                      scores on FP8 E4M3 Q and K, see
+                                      svg_quantize_qk; implies the index-map
+                                      reads of SVG_FLAG_VIRTUAL_PERMUTE */
 
 int32_t svg_abi_version(void);
 const char* svg_last_error(void);
@@ -189,7 +193,38 @@ svg_status svg_sparse_attention(const svg_geom* geom, svg_dtype in, svg_dtype ou
                                 const int32_t* ranges, const int32_t* head_order, int32_t BM,
                                 int32_t BN, int32_t flags, void* stream);
 
+/* FP8 scores, step 1: quantisation of Q and K to FP8 E4M3 (OCP "fn"
+ * encoding: bias 7, 3 mantissa bits, max 448, no infinities).  The pages
+ * only report that Sparse-vDiT composes with FP8 (Sparse-vDiT review,
+ * editorial extensions); the scheme is ours: every scale is the smallest
+ * power of two s with 448*s >= max|x| of its group (1 for an all-zero
+ * group), the values x/s are rounded to nearest E4M3, ties to even.
+ * Q: one scale per token row, q8[(b*H+h)*L + x] row x in natural order,
+ * sq[(b*H+h)*L + x].  K: one scale per tile of 64 rows of the head's working
+ * layout (token-major, row T + j*N + i, for TEMPORAL heads per `modes`;
+ * natural otherwise), k8 rows in that order, sk[(b*H+h)*ceil(L/64) + tile].
+ * q8, k8: device uint8[B*H*L*d] (16-byte aligned); sq: float[B*H*L];
+ * sk: float[B*H*ceil(L/64)].  bf16 inputs only.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED (dtype), SVG_E_HIP. */
+svg_status svg_quantize_qk(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k, svg_strides s,
+                           const int32_t* modes, uint8_t* q8, float* sq, uint8_t* k8, float* sk, void* stream);
+
+/* FP8 scores, step 2: block-banded sparse attention as svg_sparse_attention,
+ * with the scores s = (q8 . k8) * sq(row) * sk(tile) * scale from the FP8
+ * matrix cores, fp32 softmax and bf16 P.V (V bf16, strides sv).  Inputs from
+ * svg_quantize_qk with the same modes; TEMPORAL heads read Q8, V and write O
+ * through the token-major index map (k8 is already token-major).  ranges /
+ * head_order from svg_build_blocks with svg_tile_config(SVG_BF16, d).
+ * out: SVG_BF16 or SVG_F32.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED (tiles), SVG_E_HIP. */
+svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const uint8_t* q8, const float* sq,
+                                    const uint8_t* k8, const float* sk, const void* v, svg_strides sv, void* o,
+                                    svg_strides so, const int32_t* modes, const int32_t* ranges,
+                                    const int32_t* head_order, int32_t BM, int32_t BN, void* stream);
+
 /* One attention layer of the method, as a diffusion step runs it:
+ * (with SVG_FLAG_FP8_SCORES the attention is svg_quantize_qk followed by
+ * svg_sparse_attention_fp8 and no permuted copies are made)
  *   modes_in == NULL: profile on `rows` (writes labels_out, stats_out), else
  *   use modes_in (Sparse-vDiT's fixed per-head modes; no profiling, rows and
  *   stats_out unused, labels_out receives a copy of modes_in);

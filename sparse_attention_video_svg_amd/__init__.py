@@ -16,15 +16,16 @@ import os
 
 __all__ = [
     "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE", "MODE_SEARCH",
-    "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
+    "FP8_SCORES", "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
     "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
-    "svg_sparse_attention", "svg_layer_forward", "library_path",
+    "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_layer_forward", "library_path",
 ]
 
 SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
 F32, BF16 = 0, 1
 VIRTUAL_PERMUTE = 1
 MODE_SEARCH = 2  # svg_workspace_bytes: size for svg_search_modes
+FP8_SCORES = 4   # svg_layer_forward: scores on FP8 E4M3 Q and K
 SEARCH_CANDIDATES = (SKIP, WINDOW, TEMPORAL, STRIPE)  # order of svg_search_modes' stats
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -125,6 +126,8 @@ def _lib():
             "svg_layout_permute": ([g, i32, vp, S, vp, S, vp, i32, vp], i32),
             "svg_sparse_attention": ([g, i32, i32, vp, vp, vp, S, vp, vp, vp, S, vp, S, vp, S, vp, vp, vp, i32, i32,
                                       i32, vp], i32),
+            "svg_quantize_qk": ([g, i32, vp, vp, S, vp, vp, vp, vp, vp, vp], i32),
+            "svg_sparse_attention_fp8": ([g, i32, vp, vp, vp, vp, vp, S, vp, S, vp, vp, vp, i32, i32, vp], i32),
             "svg_layer_forward": ([g, i32, i32, vp, vp, vp, S, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp], i32),
         }
@@ -253,6 +256,29 @@ def svg_sparse_attention(geom, q, k, v, o, modes, ranges, head_order, qp=None, k
         ctypes.byref(g), din, _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(qp), _ptr(kp), _ptr(vp),
         _strides(qp), _ptr(o), _strides(o), _ptr(op), _strides(op), _ptr(modes), _ptr(ranges), _ptr(head_order),
         BM, BN, flags, _stream(stream)))
+
+
+def svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk, stream=None):
+    """FP8 E4M3 quantisation of Q (per row) and K (per 64-key tile of the
+    working layout): q8, k8 uint8 [B*H*L*d]; sq float32 [B*H*L]; sk float32
+    [B*H*ceil(L/64)]."""
+    _check_shape(geom, q, "q")
+    _check_shape(geom, k, "k")
+    if k.stride() != q.stride():
+        raise ValueError("q and k must share strides")
+    g = geom.c()
+    _check(_lib().svg_quantize_qk(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _strides(q), _ptr(modes),
+                                  _ptr(q8), _ptr(sq), _ptr(k8), _ptr(sk), _stream(stream)))
+
+
+def svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, head_order, stream=None):
+    _check_shape(geom, v, "v")
+    _check_shape(geom, o, "o")
+    BM, BN = svg_tile_config(BF16, geom.d)
+    g = geom.c()
+    _check(_lib().svg_sparse_attention_fp8(ctypes.byref(g), _dtype_code(o), _ptr(q8), _ptr(sq), _ptr(k8), _ptr(sk),
+                                           _ptr(v), _strides(v), _ptr(o), _strides(o), _ptr(modes), _ptr(ranges),
+                                           _ptr(head_order), BM, BN, _stream(stream)))
 
 
 def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_out=None, modes_in=None,

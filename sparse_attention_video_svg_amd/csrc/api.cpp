@@ -135,7 +135,18 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
   off = align256(off + sizeof(int32_t) * (size_t)BH);
   w.perm = off;
   w.perm_tensor_bytes = 0;
-  if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
+  if (flags & SVG_FLAG_FP8_SCORES) {  // quantised Q, K and scales; no permuted copies
+    const size_t n8 = align256((size_t)BH * g.L * g.d);
+    const int64_t nKT = (g.L + kBN_bf16 - 1) / kBN_bf16;
+    w.q8 = off;
+    off += n8;
+    w.k8 = off;
+    off += n8;
+    w.sq = off;
+    off = align256(off + sizeof(float) * (size_t)BH * g.L);
+    w.sk = off;
+    off = align256(off + sizeof(float) * (size_t)BH * nKT);
+  } else if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
     // token-major Q, K, V in the input dtype, then O sized for fp32 output
     w.perm_tensor_bytes = align256((size_t)BH * g.L * g.d * elt_bytes(dtype));
     off += 3 * w.perm_tensor_bytes + align256((size_t)BH * g.L * g.d * 4);
@@ -294,10 +305,10 @@ svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_
   if (!bytes) return fail(SVG_E_INVALID, "bytes is NULL");
   if (n_rows < 0 || (int64_t)n_rows > (int64_t)g.N * g.F)
     return fail(SVG_E_INVALID, "n_rows=%d must be in [0, N*F]", n_rows);
-  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH))
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH | SVG_FLAG_FP8_SCORES))
     return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
-  if ((flags & SVG_FLAG_MODE_SEARCH) && dtype != SVG_BF16)
-    return fail(SVG_E_UNSUPPORTED, "the mode search takes bf16 inputs");
+  if ((flags & (SVG_FLAG_MODE_SEARCH | SVG_FLAG_FP8_SCORES)) && dtype != SVG_BF16)
+    return fail(SVG_E_UNSUPPORTED, "the mode search and fp8 scores take bf16 inputs");
   *bytes = ws_layout(g, dtype, n_rows, flags).total;
   return SVG_OK;
 }
@@ -395,6 +406,49 @@ svg_status svg_sparse_attention(const svg_geom* geom, svg_dtype in, svg_dtype ou
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention");
 }
 
+svg_status svg_quantize_qk(const svg_geom* geom, svg_dtype dtype, const void* q, const void* k, svg_strides s,
+                           const int32_t* modes, uint8_t* q8, float* sq, uint8_t* k8, float* sk, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (dtype != SVG_BF16) return fail(dtype_ok(dtype) ? SVG_E_UNSUPPORTED : SVG_E_INVALID, "fp8 scores take bf16 inputs");
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(k, "k", 16));
+  TRY(check_strides(s, g, 2, "q/k"));
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(q8, "q8", 16));
+  TRY(check_ptr(k8, "k8", 16));
+  TRY(check_ptr(sq, "sq", 4));
+  TRY(check_ptr(sk, "sk", 4));
+  hipError_t e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_quantize_qk");
+}
+
+svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const uint8_t* q8, const float* sq,
+                                    const uint8_t* k8, const float* sk, const void* v, svg_strides sv, void* o,
+                                    svg_strides so, const int32_t* modes, const int32_t* ranges,
+                                    const int32_t* head_order, int32_t BM, int32_t BN, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
+  if (BM != kBM_bf16 || BN != kBN_bf16)
+    return fail(SVG_E_UNSUPPORTED, "ranges built with %dx%d tiles; this kernel needs %dx%d", BM, BN, kBM_bf16,
+                kBN_bf16);
+  TRY(check_ptr(q8, "q8", 16));
+  TRY(check_ptr(k8, "k8", 16));
+  TRY(check_ptr(sq, "sq", 4));
+  TRY(check_ptr(sk, "sk", 4));
+  TRY(check_ptr(v, "v", 16));
+  TRY(check_ptr(o, "o", 16));
+  TRY(check_strides(sv, g, 2, "v"));
+  TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(ranges, "ranges", 16));
+  TRY(check_ptr(head_order, "head_order", 4));
+  hipError_t e = launch_attention_fp8(g, q8, sq, k8, sk, v, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8");
+}
+
 svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q, const void* k,
                              const void* v, svg_strides s, void* o, svg_strides so, const int32_t* rows,
                              int32_t n_rows, float fallback_rel_mse, const int32_t* modes_in, int32_t* labels_out,
@@ -402,7 +456,11 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
   KGeom g;
   TRY(check_geom(geom, &g));
   if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
-  if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_FP8_SCORES))
+    return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  const bool fp8 = flags & SVG_FLAG_FP8_SCORES;
+  if (fp8 && in != SVG_BF16) return fail(SVG_E_UNSUPPORTED, "fp8 scores take bf16 inputs");
+  if (fp8) flags |= SVG_FLAG_VIRTUAL_PERMUTE;  // the fp8 path reads temporal heads through the index map
   const bool profile = modes_in == nullptr;
   if (profile) {
     TRY(validate_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out));
@@ -426,7 +484,7 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
   int32_t* ranges = ws_at<int32_t>(ws, w.ranges);
   int32_t* order = ws_at<int32_t>(ws, w.order);
   TRY(validate_attention(g, in, out, q, k, v, s, qp, kp, vp, sp, o, so, op, sp, profile ? labels_out : modes_in,
-                         ranges, order, BM, BN, flags));
+                         ranges, order, BM, BN, flags & SVG_FLAG_VIRTUAL_PERMUTE));
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   const int32_t* modes = modes_in;
@@ -440,6 +498,16 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
   }
   e = launch_build_blocks(g, modes, BM, BN, ranges, order, st);
   if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (blocks)");
+  if (fp8) {
+    uint8_t* q8 = ws_at<uint8_t>(ws, w.q8);
+    uint8_t* k8 = ws_at<uint8_t>(ws, w.k8);
+    float* sq = ws_at<float>(ws, w.sq);
+    float* sk = ws_at<float>(ws, w.sk);
+    e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 quantisation)");
+    e = launch_attention_fp8(g, q8, sq, k8, sk, v, s, o, so, out == SVG_BF16, modes, ranges, order, st);
+    return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
+  }
   if (!virt) {
     const void* src[3] = {q, k, v};
     void* dst[3] = {qp, kp, vp};

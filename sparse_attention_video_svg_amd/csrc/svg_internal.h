@@ -41,6 +41,7 @@ __device__ __forceinline__ int32_t fastdiv(int32_t n, uint32_t mul, uint32_t shi
 struct WsLayout {
   size_t part_acc, part_ml, row_sums, ord_x, ord_r;  // profiling
   size_t labels, ranges, order, perm, total;
+  size_t q8, k8, sq, sk;     // fp8-score path: quantised Q, K and their scales
   size_t perm_tensor_bytes;  // one permuted tensor (all heads)
   int32_t ksplit;            // key splits of the profiling sweep
 };
@@ -60,6 +61,18 @@ struct AttnPtrs {
 };
 hipError_t launch_attention_f32(const KGeom& g, const AttnPtrs& a, int32_t BM, int32_t BN, hipStream_t st);
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st);
+
+// FP8-score attention: quantisation of Q (per row) and K (per 64-key tile of
+// the working layout) to E4M3 with power-of-two scales, and the attention
+// kernel that takes them (TEMPORAL heads: Q8, V, O through the index map, K8
+// already token-major).  q8 / k8: [B*H, L, d] bytes; sq: [B*H, L];
+// sk: [B*H, ceil(L / 64)].
+hipError_t launch_quant_qk(const KGeom& g, const void* q, const void* k, svg_strides s, const int32_t* modes,
+                           uint8_t* q8, float* sq, uint8_t* k8, float* sk, hipStream_t st);
+hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const float* sq, const uint8_t* k8,
+                                const float* sk, const void* v, svg_strides sv, void* o, svg_strides so,
+                                bool out_bf16, const int32_t* modes, const int32_t* ranges, const int32_t* order,
+                                hipStream_t st);
 
 // Sampled-row sweeps (profiling, mode search): per (head, row, key slice)
 // one partial online-softmax state (m in log2 units, l, unnormalised acc) per
