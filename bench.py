@@ -69,7 +69,17 @@ def pair_count(N, F, T, mode, a1=1, a2=1, window=1, stripe=1):
 
 
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_attn_bf16_hunyuanvideo_33x3600_h24_d128.md")
-ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_video_svg_amd", "csrc", "attn_bf16.hip")
+# the bf16 attention kernel's source: its file and the headers it is built from
+ATTN_SOURCES = [os.path.join(ROOT, "sparse_attention_video_svg_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "attn_common.h", "svg_device.h", "svg_internal.h")]
+
+
+def attn_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def recorded_traffic():
@@ -79,7 +89,7 @@ def recorded_traffic():
     import hashlib
     try:
         text = open(PROFILE_SUMMARY).read()
-        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        sha = attn_source_sha256()
     except OSError:
         return None
     rec = {}
