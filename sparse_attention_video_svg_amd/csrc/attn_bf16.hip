@@ -269,11 +269,11 @@ hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf1
   return out_bf16 ? launch_attn<128, true>(g, a, nQT, grid, total, st) : launch_attn<128, false>(g, a, nQT, grid, total, st);
 }
 
-template <int D, bool VIRT>
+template <int D, bool VIRT, int W>
 static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
                               const int32_t* rows, const int32_t* ord_r, int32_t n_rows, int32_t nsplit, int32_t mode,
                               int32_t state, int32_t nstates, float* acc, float* ml, hipStream_t st) {
-  constexpr int W = kAttnWaves, S = kAttnStages;
+  constexpr int S = kAttnStages;
   const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   auto kern = k_prof_sweep<D, VIRT, W, S>;
   static bool attr_set = false;
@@ -292,6 +292,10 @@ static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, 
   return hipGetLastError();
 }
 
+// waves per workgroup of the sampled-row sweeps over short runs (4: 128 rows,
+// measured faster than 2 and 8 on the HunyuanVideo-shaped layer)
+constexpr int kProfWavesBand = 4;
+
 template <int D>
 static hipError_t launch_sweeps(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
                                 const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
@@ -299,10 +303,17 @@ static hipError_t launch_sweeps(const KGeom& g, const __bf16* q, const __bf16* k
                                 hipStream_t st) {
   for (int32_t i = 0; i < nstates; ++i) {
     hipError_t e;
+    // masks with short runs per row take workgroups of kProfWavesBand waves (fewer rows, so the union of
+    // their runs stays close to each row's own); full attention the attention kernel's 8
     if (modes[i] == SVG_TEMPORAL)
-      e = launch_prof<D, true>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, SVG_TEMPORAL, i, nstates, acc, ml, st);
+      e = launch_prof<D, true, kProfWavesBand>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, SVG_TEMPORAL, i,
+                                               nstates, acc, ml, st);
+    else if (modes[i] == SVG_FULL)
+      e = launch_prof<D, false, kAttnWaves>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates, acc,
+                                            ml, st);
     else
-      e = launch_prof<D, false>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates, acc, ml, st);
+      e = launch_prof<D, false, kProfWavesBand>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates,
+                                                acc, ml, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
