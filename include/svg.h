@@ -222,6 +222,53 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
                                     svg_strides so, const int32_t* modes, const int32_t* ranges,
                                     const int32_t* head_order, int32_t BM, int32_t BN, void* stream);
 
+/* SVG2: semantic-aware permutation ("Sparse VideoGen2 ..." explainer,
+ * 2. Methodology, A-C).  Q and K rows of each head are clustered
+ * independently by k-means into C_q / C_k clusters (Lloyd: `iters`
+ * iterations of nearest-centroid assignment, squared Euclidean, ties to the
+ * lower index, then the mean of each cluster's tokens, an empty cluster
+ * keeping its centroid); tokens are reordered so that every cluster is
+ * contiguous (stable inside a cluster); the share of query cluster a's
+ * attention on key cluster b is estimated from the centroids as
+ * n_b exp(scale * mu_a . mu_b) / sum_b' (...) (n_b: tokens of cluster b), and
+ * key clusters are taken in descending estimate (ties to the lower index)
+ * while the mass of those taken before is below p; every query token then
+ * attends exactly to the keys of its cluster's selected key clusters.
+ * Initial centroids: the tokens at floor(c * L / C), or the caller's with
+ * SVG2_FLAG_INIT_GIVEN (e.g. the previous step's, the pages' centroid cache). */
+typedef struct {
+  int32_t C_q, C_k; /* clusters of Q and of K per head, 1 .. 1024 (and <= L) */
+  int32_t iters;    /* Lloyd iterations, >= 1 */
+  float p;          /* top-p threshold of the cumulative estimated attention, > 0 */
+} svg2_params;
+
+#define SVG2_FLAG_INIT_GIVEN 1 /* mu_q / mu_k hold the initial centroids */
+
+/* Workspace of svg2_forward (also enough for svg2_kmeans with C <= max(C_q, C_k)). */
+svg_status svg2_workspace_bytes(const svg_geom* geom, const svg2_params* params, size_t* bytes);
+
+/* k-means of one tensor per head (bf16 x [B, H, L, d] with strides s):
+ * mu (device float[B*H*C*d]): initial centroids with SVG2_FLAG_INIT_GIVEN,
+ * always the final ones; labels (int32[B*H*L]) the last assignment;
+ * perm (int32[B*H*L]): token at each position of the cluster order;
+ * start (int32[B*H*(C+1)]): first position of each cluster, start[C] = L.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED, SVG_E_WORKSPACE, SVG_E_HIP. */
+svg_status svg2_kmeans(const svg_geom* geom, svg_dtype dtype, const void* x, svg_strides s, int32_t C,
+                       int32_t iters, int32_t flags, float* mu, int32_t* labels, int32_t* perm, int32_t* start,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* The SVG2 attention step: k-means of Q and of K, selection, K / V gathered
+ * into cluster order, attention over query clusters (queries read and
+ * outputs written in the caller's token order).  mu_q / mu_k: device
+ * float[B*H*C*d] (in with SVG2_FLAG_INIT_GIVEN, out always); sel (optional,
+ * device uint8[B*H*C_q*C_k]): the selection.  Only geometry fields B, H, d,
+ * N, F, T (L = T + N*F) and scale are used.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED, SVG_E_WORKSPACE, SVG_E_HIP. */
+svg_status svg2_forward(const svg_geom* geom, const svg2_params* params, svg_dtype in, svg_dtype out,
+                        const void* q, const void* k, const void* v, svg_strides s, void* o, svg_strides so,
+                        int32_t flags, float* mu_q, float* mu_k, uint8_t* sel, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* One attention layer of the method, as a diffusion step runs it:
  * (with SVG_FLAG_FP8_SCORES the attention is svg_quantize_qk followed by
  * svg_sparse_attention_fp8 and no permuted copies are made)

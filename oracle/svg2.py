@@ -37,9 +37,13 @@ def kmeans(x, C, iters, init=None):
     x = np.asarray(x, dtype=np.float64)
     mu = strided_init(x, C) if init is None else np.asarray(init, dtype=np.float64).copy()
     labels = None
+    xx = (x * x).sum(axis=1)
     for _ in range(iters):
-        dist = ((x[:, None, :] - mu[None, :, :]) ** 2).sum(axis=2)  # [L, C]
-        labels = np.argmin(dist, axis=1)  # first minimum: ties to the lower index
+        labels = np.empty(x.shape[0], dtype=np.int64)
+        mm = (mu * mu).sum(axis=1)
+        for c0 in range(0, x.shape[0], 8192):  # squared distances |x|^2 - 2 x.mu + |mu|^2, in chunks of rows
+            dist = xx[c0:c0 + 8192, None] - 2.0 * (x[c0:c0 + 8192] @ mu.T) + mm[None, :]
+            labels[c0:c0 + 8192] = np.argmin(dist, axis=1)  # first minimum: ties to the lower index
         for c in range(C):
             members = x[labels == c]
             if members.shape[0]:

@@ -19,6 +19,7 @@ __all__ = [
     "FP8_SCORES", "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
     "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
     "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_layer_forward", "library_path",
+    "Svg2Params", "SVG2_INIT_GIVEN", "svg2_workspace_bytes", "svg2_kmeans", "svg2_forward",
 ]
 
 SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
@@ -47,6 +48,26 @@ class _Geom(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("T", ctypes.c_int32), ("a1", ctypes.c_int32), ("a2", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("stripe", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _Svg2Params(ctypes.Structure):
+    _fields_ = [("C_q", ctypes.c_int32), ("C_k", ctypes.c_int32), ("iters", ctypes.c_int32), ("p", ctypes.c_float)]
+
+
+@dataclasses.dataclass
+class Svg2Params:
+    """SVG2 clustering and selection: clusters of Q and K per head, Lloyd
+    iterations, top-p threshold."""
+    C_q: int = 256
+    C_k: int = 256
+    iters: int = 3
+    p: float = 0.9
+
+    def c(self):
+        return _Svg2Params(self.C_q, self.C_k, self.iters, float(self.p))
+
+
+SVG2_INIT_GIVEN = 1
 
 
 class _Strides(ctypes.Structure):
@@ -128,6 +149,10 @@ def _lib():
                                       i32, vp], i32),
             "svg_quantize_qk": ([g, i32, vp, vp, S, vp, vp, vp, vp, vp, vp], i32),
             "svg_sparse_attention_fp8": ([g, i32, vp, vp, vp, vp, vp, S, vp, S, vp, vp, vp, i32, i32, vp], i32),
+            "svg2_workspace_bytes": ([g, P(_Svg2Params), P(ctypes.c_size_t)], i32),
+            "svg2_kmeans": ([g, i32, vp, S, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
+            "svg2_forward": ([g, P(_Svg2Params), i32, i32, vp, vp, vp, S, vp, S, i32, vp, vp, vp, vp,
+                              ctypes.c_size_t, vp], i32),
             "svg_layer_forward": ([g, i32, i32, vp, vp, vp, S, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp], i32),
         }
@@ -293,6 +318,35 @@ def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_ou
         ctypes.byref(g), _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(o),
         _strides(o), _ptr(rows), n_rows, float(fallback_rel_mse), _ptr(modes_in), _ptr(labels_out),
         _ptr(stats_out), flags, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def svg2_workspace_bytes(geom, params):
+    n = ctypes.c_size_t()
+    g, p = geom.c(), params.c()
+    _check(_lib().svg2_workspace_bytes(ctypes.byref(g), ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def svg2_kmeans(geom, x, C, iters, mu, labels, perm, start, ws, flags=0, stream=None):
+    """k-means of one [B, H, L, d] bf16 tensor per head; mu float32
+    [B*H*C*d] (initial centroids with SVG2_INIT_GIVEN), labels / perm int32
+    [B*H*L], start int32 [B*H*(C+1)]."""
+    _check_shape(geom, x, "x")
+    g = geom.c()
+    _check(_lib().svg2_kmeans(ctypes.byref(g), _dtype_code(x), _ptr(x), _strides(x), int(C), int(iters), int(flags),
+                              _ptr(mu), _ptr(labels), _ptr(perm), _ptr(start), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def svg2_forward(geom, params, q, k, v, o, mu_q, mu_k, ws, sel=None, flags=0, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    g, p = geom.c(), params.c()
+    _check(_lib().svg2_forward(ctypes.byref(g), ctypes.byref(p), _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k),
+                               _ptr(v), _strides(q), _ptr(o), _strides(o), int(flags), _ptr(mu_q), _ptr(mu_k),
+                               _ptr(sel), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def alloc_workspace(geom, dtype, n_rows=0, flags=0, device="cuda"):

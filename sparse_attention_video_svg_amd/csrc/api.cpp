@@ -284,6 +284,74 @@ int64_t mode_nnz(const KGeom& g, int32_t mode) {
   return text + video;
 }
 
+// SVG2 workspace: k-means scratch, per-tensor clustering results, selection,
+// K / V in cluster order.
+struct Svg2Ws {
+  size_t hi, lo, hn, hist, base, rank;
+  size_t mu_q, mu_k, lab_q, lab_k, perm_q, perm_k, start_q, start_k;
+  size_t sel, tiles, ntiles, rbp, kp, vp, total;
+  int32_t maxT;
+};
+
+Svg2Ws svg2_ws_layout(const KGeom& g, int32_t Cq, int32_t Ck) {
+  Svg2Ws w{};
+  const size_t BH = (size_t)g.B * g.H, L = (size_t)g.L, d = (size_t)g.d;
+  const size_t Cm = (size_t)(Cq > Ck ? Cq : Ck);
+  const size_t nBlk = (L + 255) / 256;
+  w.maxT = (int32_t)((L + kBN_bf16 - 1) / kBN_bf16 + (size_t)Ck);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  w.hi = take(BH * Cm * d * 2);
+  w.lo = take(BH * Cm * d * 2);
+  w.hn = take(BH * Cm * 4);
+  w.hist = take(BH * nBlk * Cm * 4);
+  w.base = take(BH * nBlk * Cm * 4);
+  w.rank = take(BH * L * 4);
+  w.mu_q = take(BH * (size_t)Cq * d * 4);
+  w.mu_k = take(BH * (size_t)Ck * d * 4);
+  w.lab_q = take(BH * L * 4);
+  w.lab_k = take(BH * L * 4);
+  w.perm_q = take(BH * L * 4);
+  w.perm_k = take(BH * L * 4);
+  w.start_q = take(BH * ((size_t)Cq + 1) * 4);
+  w.start_k = take(BH * ((size_t)Ck + 1) * 4);
+  w.sel = take(BH * (size_t)Cq * Ck);
+  w.tiles = take(BH * (size_t)Cq * w.maxT * 8);
+  w.ntiles = take(BH * (size_t)Cq * 4);
+  w.rbp = take(BH * ((size_t)Cq + 1) * 4);
+  w.kp = take(BH * L * d * 2);
+  w.vp = take(BH * L * d * 2);
+  w.total = off;
+  return w;
+}
+
+Svg2Scratch svg2_scratch(void* ws, const Svg2Ws& w) {
+  Svg2Scratch s;
+  s.hi = ws_at<char>(ws, w.hi);
+  s.lo = ws_at<char>(ws, w.lo);
+  s.hn = ws_at<float>(ws, w.hn);
+  s.hist = ws_at<int32_t>(ws, w.hist);
+  s.base = ws_at<int32_t>(ws, w.base);
+  s.rank = ws_at<int32_t>(ws, w.rank);
+  return s;
+}
+
+svg_status check_svg2_params(const KGeom& g, const svg2_params* prm) {
+  if (!prm) return fail(SVG_E_INVALID, "params is NULL");
+  if (prm->C_q < 1 || prm->C_k < 1) return fail(SVG_E_INVALID, "cluster counts must be >= 1");
+  if (prm->C_q > kSvg2MaxClusters || prm->C_k > kSvg2MaxClusters)
+    return fail(SVG_E_UNSUPPORTED, "cluster counts must be in [1, %d] (got %d, %d)", kSvg2MaxClusters, prm->C_q,
+                prm->C_k);
+  if (prm->C_q > g.L || prm->C_k > g.L) return fail(SVG_E_INVALID, "more clusters than tokens");
+  if (prm->iters < 1) return fail(SVG_E_INVALID, "iters must be >= 1");
+  if (!(prm->p > 0.f) || !isfinite(prm->p)) return fail(SVG_E_INVALID, "p must be finite and > 0");
+  return SVG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +515,89 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
   hipError_t e = launch_attention_fp8(g, q8, sq, k8, sk, v, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
                                       (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8");
+}
+
+svg_status svg2_workspace_bytes(const svg_geom* geom, const svg2_params* prm, size_t* bytes) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  TRY(check_svg2_params(g, prm));
+  if (!bytes) return fail(SVG_E_INVALID, "bytes is NULL");
+  *bytes = svg2_ws_layout(g, prm->C_q, prm->C_k).total;
+  return SVG_OK;
+}
+
+svg_status svg2_kmeans(const svg_geom* geom, svg_dtype dtype, const void* x, svg_strides s, int32_t C, int32_t iters,
+                       int32_t flags, float* mu, int32_t* labels, int32_t* perm, int32_t* start, void* ws,
+                       size_t ws_bytes, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (dtype != SVG_BF16) return fail(dtype_ok(dtype) ? SVG_E_UNSUPPORTED : SVG_E_INVALID, "bf16 inputs only");
+  const svg2_params prm{C, C, iters, 1.f};
+  TRY(check_svg2_params(g, &prm));
+  if (flags & ~SVG2_FLAG_INIT_GIVEN) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  TRY(check_ptr(x, "x", 16));
+  TRY(check_strides(s, g, 2, "x"));
+  TRY(check_ptr(mu, "mu", 4));
+  TRY(check_ptr(labels, "labels", 4));
+  TRY(check_ptr(perm, "perm", 4));
+  TRY(check_ptr(start, "start", 4));
+  const Svg2Ws w = svg2_ws_layout(g, C, C);
+  TRY(check_ptr(ws, "ws", 256));
+  if (ws_bytes < w.mu_q) return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.mu_q);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!(flags & SVG2_FLAG_INIT_GIVEN)) e = launch_km_init(g, x, s, C, mu, st);
+  if (e == hipSuccess) e = launch_kmeans(g, x, s, C, iters, mu, labels, perm, start, svg2_scratch(ws, w), st);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg2_kmeans");
+}
+
+svg_status svg2_forward(const svg_geom* geom, const svg2_params* prm, svg_dtype in, svg_dtype out, const void* q,
+                        const void* k, const void* v, svg_strides s, void* o, svg_strides so, int32_t flags, float* mu_q,
+                        float* mu_k, uint8_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  TRY(check_svg2_params(g, prm));
+  if (in != SVG_BF16) return fail(dtype_ok(in) ? SVG_E_UNSUPPORTED : SVG_E_INVALID, "bf16 inputs only");
+  if (!dtype_ok(out)) return fail(SVG_E_INVALID, "unknown output dtype");
+  if (flags & ~SVG2_FLAG_INIT_GIVEN) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(k, "k", 16));
+  TRY(check_ptr(v, "v", 16));
+  TRY(check_ptr(o, "o", 16));
+  TRY(check_strides(s, g, 2, "q/k/v"));
+  TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_ptr(mu_q, "mu_q", 4));
+  TRY(check_ptr(mu_k, "mu_k", 4));
+  const Svg2Ws w = svg2_ws_layout(g, prm->C_q, prm->C_k);
+  TRY(check_ptr(ws, "ws", 256));
+  if (ws_bytes < w.total) return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+  const Svg2Scratch sc = svg2_scratch(ws, w);
+  int32_t* lab_q = ws_at<int32_t>(ws, w.lab_q);
+  int32_t* lab_k = ws_at<int32_t>(ws, w.lab_k);
+  int32_t* perm_q = ws_at<int32_t>(ws, w.perm_q);
+  int32_t* perm_k = ws_at<int32_t>(ws, w.perm_k);
+  int32_t* start_q = ws_at<int32_t>(ws, w.start_q);
+  int32_t* start_k = ws_at<int32_t>(ws, w.start_k);
+  uint8_t* sel_w = sel ? sel : ws_at<uint8_t>(ws, w.sel);
+  hipError_t e = hipSuccess;
+  if (!(flags & SVG2_FLAG_INIT_GIVEN)) {
+    e = launch_km_init(g, q, s, prm->C_q, mu_q, st);
+    if (e == hipSuccess) e = launch_km_init(g, k, s, prm->C_k, mu_k, st);
+  }
+  if (e == hipSuccess) e = launch_kmeans(g, q, s, prm->C_q, prm->iters, mu_q, lab_q, perm_q, start_q, sc, st);
+  if (e == hipSuccess) e = launch_kmeans(g, k, s, prm->C_k, prm->iters, mu_k, lab_k, perm_k, start_k, sc, st);
+  if (e == hipSuccess)
+    e = launch_svg2_select(g, prm->C_q, prm->C_k, prm->p, mu_q, mu_k, start_q, start_k, sel_w,
+                           ws_at<char>(ws, w.tiles), ws_at<int32_t>(ws, w.ntiles), w.maxT, ws_at<int32_t>(ws, w.rbp),
+                           st);
+  if (e == hipSuccess) e = launch_gather_rows(g, k, s, perm_k, ws_at<char>(ws, w.kp), st);
+  if (e == hipSuccess) e = launch_gather_rows(g, v, s, perm_k, ws_at<char>(ws, w.vp), st);
+  if (e == hipSuccess)
+    e = launch_svg2_attention(g, q, s, ws_at<char>(ws, w.kp), ws_at<char>(ws, w.vp), o, so, out == SVG_BF16, perm_q,
+                              start_q, ws_at<int32_t>(ws, w.rbp), ws_at<char>(ws, w.tiles),
+                              ws_at<int32_t>(ws, w.ntiles), prm->C_q, w.maxT, st);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg2_forward");
 }
 
 svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q, const void* k,

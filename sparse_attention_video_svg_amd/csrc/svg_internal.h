@@ -74,6 +74,31 @@ hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const float* 
                                 bool out_bf16, const int32_t* modes, const int32_t* ranges, const int32_t* order,
                                 hipStream_t st);
 
+// SVG2 (semantic-aware permutation): k-means of one tensor per head
+// (`iters` Lloyd iterations from the centroids in mu, which are updated in
+// place), the stable cluster order (perm, start), the centroid-score top-p
+// selection with tile lists, the gather of K / V into cluster order, and the
+// attention over query clusters.  Scratch of the k-means:
+struct Svg2Scratch {
+  void *hi, *lo;          // bf16 [BH][C][d]: centroid and its residual
+  float* hn;              // [BH][C]: 0.5 |mu|^2
+  int32_t *hist, *base;   // [BH][ceil(L/256)][C]
+  int32_t* rank;          // [BH][L]
+};
+constexpr int32_t kSvg2MaxClusters = 1024;
+hipError_t launch_km_init(const KGeom& g, const void* x, svg_strides s, int32_t C, float* mu, hipStream_t st);
+hipError_t launch_kmeans(const KGeom& g, const void* x, svg_strides s, int32_t C, int32_t iters, float* mu,
+                         int32_t* labels, int32_t* perm, int32_t* start, const Svg2Scratch& w, hipStream_t st);
+hipError_t launch_svg2_select(const KGeom& g, int32_t Cq, int32_t Ck, float p, const float* mu_q, const float* mu_k,
+                              const int32_t* start_q, const int32_t* start_k, uint8_t* sel, void* tiles,
+                              int32_t* ntiles, int32_t maxT, int32_t* rb_prefix, hipStream_t st);
+hipError_t launch_gather_rows(const KGeom& g, const void* src, svg_strides s, const int32_t* perm, void* dst,
+                              hipStream_t st);
+hipError_t launch_svg2_attention(const KGeom& g, const void* q, svg_strides s, const void* kp, const void* vp, void* o,
+                                 svg_strides so, bool out_bf16, const int32_t* perm_q, const int32_t* start_q,
+                                 const int32_t* rb_prefix, const void* tiles, const int32_t* ntiles, int32_t Cq,
+                                 int32_t maxT, hipStream_t st);
+
 // Sampled-row sweeps (profiling, mode search): per (head, row, key slice)
 // one partial online-softmax state (m in log2 units, l, unnormalised acc) per
 // mask, at slot ((bh * n_rows + row) * ksplit + slice) * nstates + state.

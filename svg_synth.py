@@ -168,3 +168,29 @@ def small_config(N, F, T, H, d, a1, a2, kinds, seed, signal=1.5, noise=1.0, dtyp
     if dtype == "bf16":
         q, k, v = (bf16_to_f32(bf16_bits(a)) for a in (q, k, v))
     return dict(q=q, k=k, v=v, kinds=np.asarray(kinds, dtype=np.int32), cfg=c)
+
+
+def svg2_inputs(N, F, T, H, d, G, seed, spread=1.0, noise=0.3, dtype="bf16"):
+    """Inputs for the SVG2 path: per head, G semantic groups with centres
+    ~ N(0, spread^2) in d dimensions; every token belongs to a group drawn
+    uniformly at random (groups are scattered over positions, not frames);
+    its query and key are the group centre plus independent N(0, noise^2)
+    noise, its value iid N(0, 1).  Draw order per head (own stream
+    default_rng([seed, h + 1])): centres, groups, q-noise, k-noise, v."""
+    L = T + N * F
+    q = np.empty((H, L, d), dtype=np.float32)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    groups = np.empty((H, L), dtype=np.int64)
+    centres = np.empty((H, G, d), dtype=np.float32)
+    for h in range(H):
+        rng = np.random.default_rng([seed, h + 1])
+        c = rng.standard_normal((G, d), dtype=np.float32) * spread
+        g = rng.integers(0, G, L)
+        q[h] = c[g] + noise * rng.standard_normal((L, d), dtype=np.float32)
+        k[h] = c[g] + noise * rng.standard_normal((L, d), dtype=np.float32)
+        v[h] = rng.standard_normal((L, d), dtype=np.float32)
+        groups[h], centres[h] = g, c
+    if dtype == "bf16":
+        q, k, v = (bf16_to_f32(bf16_bits(a)) for a in (q, k, v))
+    return dict(q=q, k=k, v=v, groups=groups, centres=centres)

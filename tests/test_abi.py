@@ -19,7 +19,7 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(svg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(svg2?_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", svg.library_path()], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (svg_\w+)", out))
+    exported = set(re.findall(r"\bT (svg2?_\w+)", out))
     assert set(declared_functions()) <= exported
     assert svg.svg_abi_version() == 1
 
@@ -201,3 +201,45 @@ def test_search_validation():
     with pytest.raises(svg.SvgError) as e:
         svg.svg_workspace_bytes(gg, svg.F32, 16, svg.MODE_SEARCH)
     assert e.value.status == E_UNSUPPORTED
+
+
+def test_svg2_validation():
+    g = geom().c()
+    L = raw()
+    s = strides()
+    gg = geom()
+    need = svg.svg2_workspace_bytes(gg, svg.Svg2Params(32, 48, 2, 0.9))
+    assert need > svg.svg2_workspace_bytes(gg, svg.Svg2Params(32, 32, 2, 0.9))
+    base = dict(Cq=32, Ck=48, it=2, p=0.9, din=svg.BF16, dout=svg.BF16, flags=0, mq=A, mk=A, ws=A, wsb=need)
+
+    def fwd(**kw):
+        a = dict(base)
+        a.update(kw)
+        prm = svg._Svg2Params(a["Cq"], a["Ck"], a["it"], a["p"])
+        return L.svg2_forward(ctypes.byref(g), ctypes.byref(prm), a["din"], a["dout"], A, A, A, s, A, s, a["flags"],
+                              a["mq"], a["mk"], None, a["ws"], a["wsb"], None)
+
+    assert fwd(Cq=0) == E_INVALID
+    assert fwd(Ck=1025) == E_UNSUPPORTED
+    assert fwd(Cq=gg.L + 1) in (E_INVALID, E_UNSUPPORTED)
+    assert fwd(it=0) == E_INVALID
+    assert fwd(p=0.0) == E_INVALID
+    assert fwd(p=float("nan")) == E_INVALID
+    assert fwd(din=svg.F32) == E_UNSUPPORTED
+    assert fwd(dout=9) == E_INVALID
+    assert fwd(flags=2) == E_INVALID
+    assert fwd(mq=None) == E_INVALID
+    assert fwd(mk=None) == E_INVALID
+    assert fwd(ws=A + 16) == E_INVALID
+    assert fwd(wsb=need - 1) == E_WORKSPACE
+
+    def km(C=32, it=2, flags=0, wsb=need, dt=svg.BF16, mu=A, lab=A, perm=A, start=A):
+        return L.svg2_kmeans(ctypes.byref(g), dt, A, s, C, it, flags, mu, lab, perm, start, A, wsb, None)
+
+    assert km(C=0) == E_INVALID
+    assert km(it=0) == E_INVALID
+    assert km(flags=4) == E_INVALID
+    assert km(dt=svg.F32) == E_UNSUPPORTED
+    assert km(mu=None) == E_INVALID and km(lab=None) == E_INVALID
+    assert km(perm=None) == E_INVALID and km(start=None) == E_INVALID
+    assert km(wsb=16) == E_WORKSPACE
