@@ -189,6 +189,65 @@ def time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch):
             "search_modes": {nm: int((m == c).sum()) for c, nm in names.items()}}
 
 
+def time_svg2(args, svg, S, cfg, dev, np, torch):
+    """svg2_forward (k-means of Q and K from the strided start, selection,
+    K/V gather, attention) on SVG2-shaped inputs of the same geometry: 256
+    planted semantic groups per head, C_q = C_k = 256, 3 Lloyd iterations,
+    p = 0.9."""
+    C, iters, p = 256, 3, 0.9
+    g = svg.Geom(B=1, H=cfg["H"], d=cfg["d"], N=cfg["N"], F=cfg["F"], T=cfg["T"])
+    H, d, L = g.H, g.d, g.L
+    t0 = time.time()
+    inp = S.svg2_inputs(g.N, g.F, g.T, H, d, C, seed=31, spread=args.svg2_spread)
+    log(f"svg2 inputs generated in {time.time() - t0:.1f} s")
+    q, k, v = (torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16)[None] for n in "qkv")
+    del inp
+    o = torch.empty_like(q)
+    prm = svg.Svg2Params(C, C, iters, p)
+    mq = torch.empty(H * C * d, dtype=torch.float32, device=dev)
+    mk = torch.empty_like(mq)
+    sel = torch.empty(H * C * C, dtype=torch.uint8, device=dev)
+    ws = torch.empty(svg.svg2_workspace_bytes(g, prm), dtype=torch.uint8, device=dev)
+    lab = torch.empty(H * L, dtype=torch.int32, device=dev)
+    perm = torch.empty_like(lab)
+    start = torch.empty(H * (C + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    fwd_ms = timed(lambda: svg.svg2_forward(g, prm, q, k, v, o, mq, mk, ws, sel=sel))
+    log(f"svg2 forward: {fwd_ms:.3f} ms")
+    counts = []
+    for x in (q, k):
+        svg.svg2_kmeans(g, x, C, iters, mq, lab, perm, start, ws)
+        st = start.cpu().numpy().reshape(H, C + 1)
+        counts.append(np.diff(st, axis=1).astype(np.float64))
+    km_ms = timed(lambda: (svg.svg2_kmeans(g, q, C, iters, mq, lab, perm, start, ws),
+                           svg.svg2_kmeans(g, k, C, iters, mk, lab, perm, start, ws)))
+    sl = sel.cpu().numpy().reshape(H, C, C).astype(np.float64)
+    pairs = float(np.einsum("ha,hab,hb->", counts[0], sl, counts[1]))
+    flops = 4.0 * d * pairs
+    rest_ms = fwd_ms - km_ms
+    log(f"svg2 k-means (Q and K): {km_ms:.3f} ms, density {pairs / (H * L * L):.4f}")
+    return {"svg2_ms": round(fwd_ms, 4), "svg2_kmeans_ms": round(km_ms, 4),
+            "svg2_select_gather_attn_ms": round(rest_ms, 4),
+            "svg2_density": round(pairs / (H * L * L), 4),
+            "svg2_effective_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 2),
+            "svg2_attn_tflops_est": round(flops / (rest_ms * 1e-3) / 1e12, 2) if rest_ms > 0 else None,
+            "svg2_config": {"clusters_q": C, "clusters_k": C, "iters": iters, "p": p, "init": "strided",
+                            "planted_groups": C, "spread": args.svg2_spread, "noise": 0.3}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +262,9 @@ def main():
     ap.add_argument("--search", action="store_true", help="also time svg_search_modes on the same inputs")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 E4M3 scores: quantise Q, K (svg_quantize_qk) and run svg_sparse_attention_fp8")
+    ap.add_argument("--svg2", action="store_true",
+                    help="also time svg2_forward (SVG2 semantic-aware permutation) on the same geometry")
+    ap.add_argument("--svg2-spread", type=float, default=1.0, help="spread of the planted SVG2 group centres")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by head with no "
@@ -364,6 +426,9 @@ def main():
     }
     if args.search and bf16:
         result.update(time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch))
+    if args.svg2 and bf16:
+        del qp, kp, vp, op
+        result.update(time_svg2(args, svg, S, cfg, dev, np, torch))
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, lab, d, 1.0 / np.sqrt(d))

@@ -289,8 +289,7 @@ int64_t mode_nnz(const KGeom& g, int32_t mode) {
 struct Svg2Ws {
   size_t hi, lo, hn, hist, base, rank;
   size_t mu_q, mu_k, lab_q, lab_k, perm_q, perm_k, start_q, start_k;
-  size_t sel, tiles, ntiles, rbp, kp, vp, total;
-  int32_t maxT;
+  size_t sel, segs, nseg, nkeys, ord, rbp, kp, vp, total;
 };
 
 Svg2Ws svg2_ws_layout(const KGeom& g, int32_t Cq, int32_t Ck) {
@@ -298,7 +297,6 @@ Svg2Ws svg2_ws_layout(const KGeom& g, int32_t Cq, int32_t Ck) {
   const size_t BH = (size_t)g.B * g.H, L = (size_t)g.L, d = (size_t)g.d;
   const size_t Cm = (size_t)(Cq > Ck ? Cq : Ck);
   const size_t nBlk = (L + 255) / 256;
-  w.maxT = (int32_t)((L + kBN_bf16 - 1) / kBN_bf16 + (size_t)Ck);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -320,8 +318,10 @@ Svg2Ws svg2_ws_layout(const KGeom& g, int32_t Cq, int32_t Ck) {
   w.start_q = take(BH * ((size_t)Cq + 1) * 4);
   w.start_k = take(BH * ((size_t)Ck + 1) * 4);
   w.sel = take(BH * (size_t)Cq * Ck);
-  w.tiles = take(BH * (size_t)Cq * w.maxT * 8);
-  w.ntiles = take(BH * (size_t)Cq * 4);
+  w.segs = take(BH * (size_t)Cq * Ck * 8);
+  w.nseg = take(BH * (size_t)Cq * 4);
+  w.nkeys = take(BH * (size_t)Cq * 4);
+  w.ord = take(BH * (size_t)Cq * 4);
   w.rbp = take(BH * ((size_t)Cq + 1) * 4);
   w.kp = take(BH * L * d * 2);
   w.vp = take(BH * L * d * 2);
@@ -589,14 +589,14 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* prm, svg_dtype 
   if (e == hipSuccess) e = launch_kmeans(g, k, s, prm->C_k, prm->iters, mu_k, lab_k, perm_k, start_k, sc, st);
   if (e == hipSuccess)
     e = launch_svg2_select(g, prm->C_q, prm->C_k, prm->p, mu_q, mu_k, start_q, start_k, sel_w,
-                           ws_at<char>(ws, w.tiles), ws_at<int32_t>(ws, w.ntiles), w.maxT, ws_at<int32_t>(ws, w.rbp),
-                           st);
+                           ws_at<char>(ws, w.segs), ws_at<int32_t>(ws, w.nseg), ws_at<int32_t>(ws, w.nkeys),
+                           ws_at<int32_t>(ws, w.ord), ws_at<int32_t>(ws, w.rbp), st);
   if (e == hipSuccess) e = launch_gather_rows(g, k, s, perm_k, ws_at<char>(ws, w.kp), st);
   if (e == hipSuccess) e = launch_gather_rows(g, v, s, perm_k, ws_at<char>(ws, w.vp), st);
   if (e == hipSuccess)
     e = launch_svg2_attention(g, q, s, ws_at<char>(ws, w.kp), ws_at<char>(ws, w.vp), o, so, out == SVG_BF16, perm_q,
-                              start_q, ws_at<int32_t>(ws, w.rbp), ws_at<char>(ws, w.tiles),
-                              ws_at<int32_t>(ws, w.ntiles), prm->C_q, w.maxT, st);
+                              start_q, ws_at<int32_t>(ws, w.ord), ws_at<int32_t>(ws, w.rbp), ws_at<char>(ws, w.segs),
+                              ws_at<int32_t>(ws, w.nseg), ws_at<int32_t>(ws, w.nkeys), prm->C_q, prm->C_k, st);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg2_forward");
 }
 

@@ -125,7 +125,8 @@ __device__ __forceinline__ f32x16 score_block(const __bf16* lds_k, const bf16x8*
 // Both 32-key blocks of a tile, the two accumulation chains interleaved and
 // the K fragments read kAhead steps before their MFMAs, so LDS latency hides
 // behind matrix work instead of stalling every pair of MFMAs.
-template <int D>
+// With ACC the products are added to s0, s1 instead of replacing them.
+template <int D, bool ACC = false>
 __device__ __forceinline__ void score_tile(const __bf16* lds_k, const bf16x8* qf, int lane, f32x16& s0, f32x16& s1) {
   using C = TileCfg<D>;
   constexpr int KS = D / 16, kAhead = 3;
@@ -141,8 +142,10 @@ __device__ __forceinline__ void score_tile(const __bf16* lds_k, const bf16x8* qf
     f0[ks] = rd(m0, sw0, ks);
     f1[ks] = rd(m1, sw1, ks);
   }
-  s0 = f32x16{};
-  s1 = f32x16{};
+  if (!ACC) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+  }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (ks + kAhead < KS) {

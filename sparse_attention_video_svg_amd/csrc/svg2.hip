@@ -66,14 +66,18 @@ __global__ void k_km_split(int32_t C, int32_t D, const float* __restrict__ mu, _
   if (t == 0) hn[(int64_t)bh * C + c] = 0.5f * s;
 }
 
-// grid (ceil(L/256), BH), 8 waves x 32 tokens.  labels[bh*L + x].
+// grid (ceil(L/256), BH), 8 waves x 32 tokens.  labels[bh*L + x].  The
+// scores x . hi and x . lo accumulate into one register pair; the half
+// squared norms sit in LDS; two workgroups share a CU, so one's loads
+// overlap the other's matrix work.
 template <int D>
-__global__ __launch_bounds__(512, 1) void k_km_assign(KGeom g, const __bf16* __restrict__ x, svg_strides s,
+__global__ __launch_bounds__(512, 4) void k_km_assign(KGeom g, const __bf16* __restrict__ x, svg_strides s,
                                                       int32_t C, const __bf16* __restrict__ hi,
                                                       const __bf16* __restrict__ lo, const float* __restrict__ hn,
                                                       int32_t* __restrict__ labels) {
   using TC = TileCfg<D, 8>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][TC::TILE_ELEMS];  // [stage][hi, lo]
+  __shared__ float hns[kSvg2MaxClusters];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y;
@@ -85,6 +89,7 @@ __global__ __launch_bounds__(512, 1) void k_km_assign(KGeom g, const __bf16* __r
   const int nct = (C + kBN - 1) / kBN;
   lh.template load1<0>(g, 0, lds[0][0], wave, lane);
   ll.template load1<0>(g, 0, lds[0][1], wave, lane);
+  for (int c = tid; c < C; c += 512) hns[c] = hn[cb + c];
 
   const int tok = blockIdx.x * kKmRows + wave * 32 + (lane & 31);
   const bool valid = tok < g.L;
@@ -100,16 +105,16 @@ __global__ __launch_bounds__(512, 1) void k_km_assign(KGeom g, const __bf16* __r
       lh.template load1<0>(g, (ct + 1) * kBN, lds[sg ^ 1][0], wave, lane);
       ll.template load1<0>(g, (ct + 1) * kBN, lds[sg ^ 1][1], wave, lane);
     }
-    f32x16 a0, a1, b0, b1;
+    f32x16 a0, a1;
     score_tile<D>(lds[sg][0], qf, lane, a0, a1);
-    score_tile<D>(lds[sg][1], qf, lane, b0, b1);
+    score_tile<D, true>(lds[sg][1], qf, lane, a0, a1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int c = ct * kBN + acc_key(kb2, r, hh);
         if (c < C) {
-          const float v = (kb2 ? a1[r] + b1[r] : a0[r] + b0[r]) - hn[cb + c];
+          const float v = (kb2 ? a1[r] : a0[r]) - hns[c];
           if (v > best || (v == best && c < bidx)) {
             best = v;
             bidx = c;
@@ -149,35 +154,47 @@ __global__ __launch_bounds__(256) void k_km_hist(int32_t L, int32_t C, int32_t n
 }
 
 // grid (BH), 1024 threads: cluster totals, starts (start[C] = L) and the
-// base position of every (block, cluster) in the cluster order.
+// base position of every (block, cluster) in the cluster order.  Thread
+// (part, c) walks part of the histogram blocks of cluster c (P = 1024 / C
+// parts of consecutive blocks).
 __global__ __launch_bounds__(1024) void k_km_scan(int32_t L, int32_t C, int32_t nBlk, const int32_t* __restrict__ hist,
                                                   int32_t* __restrict__ base, int32_t* __restrict__ start) {
-  __shared__ int sc[1024];
-  const int bh = blockIdx.x, c = threadIdx.x;
+  __shared__ int sc[1024], pt[1024];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int P = 1024 / C;
+  const int c = tid % C, part = tid / C;
+  const bool act = part < P;
+  const int b0 = act ? (int)((int64_t)part * nBlk / P) : 0, b1 = act ? (int)((int64_t)(part + 1) * nBlk / P) : 0;
   const int64_t hb = (int64_t)bh * nBlk * C;
   int tot = 0;
-  if (c < C)
-    for (int blk = 0; blk < nBlk; ++blk) tot += hist[hb + (int64_t)blk * C + c];
-  sc[c] = c < C ? tot : 0;
+#pragma unroll 8
+  for (int blk = b0; blk < b1; ++blk) tot += hist[hb + (int64_t)blk * C + c];
+  pt[tid] = tot;  // part totals, [part][c]
+  __syncthreads();
+  int ctot = 0;
+  if (tid < C)
+    for (int q = 0; q < P; ++q) ctot += pt[q * C + tid];
+  sc[tid] = tid < C ? ctot : 0;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-    const int v = c >= o ? sc[c - o] : 0;
+    const int v = tid >= o ? sc[tid - o] : 0;
     __syncthreads();
-    sc[c] += v;
+    sc[tid] += v;
     __syncthreads();
   }
-  const int st = sc[c] - (c < C ? tot : 0);
-  if (c < C) {
-    start[(int64_t)bh * (C + 1) + c] = st;
-    int run = st;
-    for (int blk = 0; blk < nBlk; ++blk) {
+  if (tid < C) start[(int64_t)bh * (C + 1) + tid] = sc[tid] - ctot;
+  if (tid == 0) start[(int64_t)bh * (C + 1) + C] = L;
+  if (act) {
+    int run = (c > 0 ? sc[c - 1] : 0);
+    for (int q = 0; q < part; ++q) run += pt[q * C + c];
+#pragma unroll 8
+    for (int blk = b0; blk < b1; ++blk) {
       const int64_t o = hb + (int64_t)blk * C + c;
       const int hcount = hist[o];
       base[o] = run;
       run += hcount;
     }
   }
-  if (c == 0) start[(int64_t)bh * (C + 1) + C] = L;
 }
 
 // grid (nBlk, BH), 256 threads: perm[bh*L + position] = token.
@@ -193,36 +210,95 @@ __global__ __launch_bounds__(256) void k_km_scatter(int32_t L, int32_t C, int32_
   perm[(int64_t)bh * L + pos] = xi;
 }
 
-// grid (C, BH), D threads: mu = mean of the cluster's tokens, summed in
-// cluster order (an empty cluster keeps its centroid).
-__global__ void k_km_update(KGeom g, const __bf16* __restrict__ x, svg_strides s, int32_t C,
-                            const int32_t* __restrict__ perm, const int32_t* __restrict__ start,
-                            float* __restrict__ mu) {
-  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+// grid (C, BH), 256 threads: mu = mean of the cluster's tokens (an empty
+// cluster keeps its centroid).  Wave w takes the 64-position chunks w, w+4,
+// ... of the cluster: one coalesced load of the chunk's token ids, then row
+// gathers 8 at a time (each lane two dims of one row; D = 64: two rows per
+// step), into 8 partial sums.  The partials combine in a fixed order: the
+// result does not depend on scheduling.
+template <int D>
+__global__ __launch_bounds__(256) void k_km_update(KGeom g, const __bf16* __restrict__ x, svg_strides s, int32_t C,
+                                                   const int32_t* __restrict__ perm,
+                                                   const int32_t* __restrict__ start, float* __restrict__ mu) {
+  constexpr int HALF = D / 2;      // lanes per token row (two dims each)
+  constexpr int TPW = 64 / HALF;   // token rows per wave and step
+  constexpr int U = 8;
+  __shared__ float2 part[4][64];
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int dp = lane % HALF, ts = lane / HALF;
   const int b = bh / g.H, h = bh % g.H;
-  const __bf16* xb = x + (int64_t)b * s.b + (int64_t)h * s.h + t;
+  const __bf16* xb = x + (int64_t)b * s.b + (int64_t)h * s.h + 2 * dp;
+  const int32_t* pp = perm + (int64_t)bh * g.L;
   const int64_t sb = (int64_t)bh * (C + 1);
   const int i0 = start[sb + c], i1 = start[sb + c + 1];
   if (i1 <= i0) return;
-  float sum = 0.f;
-  for (int i = i0; i < i1; ++i) sum += (float)xb[(int64_t)perm[(int64_t)bh * g.L + i] * s.x];
-  mu[((int64_t)bh * C + c) * g.d + t] = sum / (float)(i1 - i0);
+  float2 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = make_float2(0.f, 0.f);
+  for (int chunk = i0 + w * 64; chunk < i1; chunk += 4 * 64) {
+    const int n = min(64, i1 - chunk);
+    const int ids = pp[chunk + min(lane, n - 1)];
+    for (int k = 0; k < n; k += U * TPW) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = k + u * TPW + ts;
+        const int tk = __shfl(ids, min(e, n - 1));
+        const bf16x2 v = *reinterpret_cast<const bf16x2*>(xb + (int64_t)tk * s.x);
+        acc[u].x += e < n ? (float)v[0] : 0.f;
+        acc[u].y += e < n ? (float)v[1] : 0.f;
+      }
+    }
+  }
+  float2 t;
+  t.x = ((acc[0].x + acc[1].x) + (acc[2].x + acc[3].x)) + ((acc[4].x + acc[5].x) + (acc[6].x + acc[7].x));
+  t.y = ((acc[0].y + acc[1].y) + (acc[2].y + acc[3].y)) + ((acc[4].y + acc[5].y) + (acc[6].y + acc[7].y));
+  if (TPW == 2) {  // the two token rows of a wave step; a + b == b + a, so both halves agree
+    t.x += __shfl_xor(t.x, 32);
+    t.y += __shfl_xor(t.y, 32);
+  }
+  part[w][lane] = t;
+  __syncthreads();
+  if (w == 0 && lane < HALF) {
+    const float2 r0 = part[0][lane], r1 = part[1][lane], r2 = part[2][lane], r3 = part[3][lane];
+    const float n = (float)(i1 - i0);
+    float* m = mu + ((int64_t)bh * C + c) * D + 2 * lane;
+    m[0] = ((r0.x + r1.x) + (r2.x + r3.x)) / n;
+    m[1] = ((r0.y + r1.y) + (r2.y + r3.y)) / n;
+  }
 }
 
-// grid (Cq, BH), 256 threads.  sel[(bh*Cq + a)*Ck + b]; tiles / ntiles: the
-// selected key clusters' keys in cluster order as ranges of <= 64 keys.
+// grid (Cq, BH), 256 threads.  sel[(bh*Cq + a)*Ck + b]; the selected key
+// clusters of a as segments of the cluster order, ascending b:
+// segs[(bh*Cq + a)*Ck + i] = (first key position of the i-th selected
+// cluster, its offset in the concatenation of the selected clusters' keys);
+// nseg / nkeys[bh*Cq + a]: segments and keys in total.
 __global__ __launch_bounds__(256) void k_svg2_select(KGeom g, int32_t Cq, int32_t Ck, float p,
                                                      const float* __restrict__ mu_q, const float* __restrict__ mu_k,
                                                      const int32_t* __restrict__ start_k, uint8_t* __restrict__ sel,
-                                                     int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                     int32_t maxT) {
-  __shared__ float P[1024], srt[1024], red[256];
-  __shared__ int tsc[1024];
+                                                     int2* __restrict__ segs, int32_t* __restrict__ nseg,
+                                                     int32_t* __restrict__ nkeys) {
+  __shared__ float P[1024], srt[1024], red[256], zs[1024];
+  __shared__ int tsc[1024], vst[1024];
   const int a = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
   const int D = g.d;
   const float* mq = mu_q + ((int64_t)bh * Cq + a) * D;
   const int64_t sk = (int64_t)bh * (Ck + 1);
   constexpr int PER = 4;  // clusters per thread (Ck <= 1024)
+  // centroid dot products: wave wv takes key clusters wv, wv + 4, ...; the
+  // lanes split the dims (lane, lane + 64), a fixed butterfly sums them
+  {
+    const float q0 = mq[lane], q1 = D > 64 ? mq[lane + 64] : 0.f;
+    for (int bb = wv; bb < Ck; bb += 4) {
+      const float* mk = mu_k + ((int64_t)bh * Ck + bb) * D;
+      float dot = q0 * mk[lane];
+      if (D > 64) dot = __builtin_fmaf(q1, mk[lane + 64], dot);
+      dot = wave_sum(dot);
+      if (lane == 0) zs[bb] = dot;
+    }
+  }
+  __syncthreads();
   float z[PER];
   float m = -INFINITY;
 #pragma unroll
@@ -230,10 +306,7 @@ __global__ __launch_bounds__(256) void k_svg2_select(KGeom g, int32_t Cq, int32_
     const int bb = t + 256 * i;
     z[i] = -INFINITY;
     if (bb < Ck && start_k[sk + bb + 1] > start_k[sk + bb]) {
-      const float* mk = mu_k + ((int64_t)bh * Ck + bb) * D;
-      float dot = 0.f;
-      for (int e = 0; e < D; ++e) dot = __builtin_fmaf(mq[e], mk[e], dot);
-      z[i] = g.scale * dot;
+      z[i] = g.scale * zs[bb];
       m = fmaxf(m, z[i]);
     }
   }
@@ -301,56 +374,81 @@ __global__ __launch_bounds__(256) void k_svg2_select(KGeom g, int32_t Cq, int32_
     if (r < Ck) srt[r] = off + loc[i];  // mass of the clusters ranked before r
   }
   __syncthreads();
-  // selection and tile counts, then tile offsets in ascending cluster order
-  int nt[PER], tot = 0;
+  // selection, then each selected cluster's segment index and key offset in
+  // ascending cluster order
+  int nsel[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int bb = t + 256 * i;
-    nt[i] = 0;
+    nsel[i] = 0;
     if (bb < Ck) {
       const int n = start_k[sk + bb + 1] - start_k[sk + bb];
       const bool s = n > 0 && srt[rk[i]] < p;
       sel[((int64_t)bh * Cq + a) * Ck + bb] = s ? 1 : 0;
-      nt[i] = s ? (n + kBN - 1) / kBN : 0;
+      nsel[i] = s ? n : 0;
     }
+    tsc[bb] = nsel[i];
   }
-  // tile offsets: cluster bb = t + 256 i; scan over the order (i, t)
-#pragma unroll
-  for (int i = 0; i < PER; ++i) tsc[t + 256 * i] = nt[i];
   __syncthreads();
   if (t == 0) {
-    int acc = 0;
+    int ns = 0, nk = 0;
     for (int bb = 0; bb < Ck; ++bb) {
-      const int v = tsc[bb];
-      tsc[bb] = acc;
-      acc += v;
+      const int n = tsc[bb];
+      tsc[bb] = ns;
+      vst[bb] = nk;
+      ns += n > 0;
+      nk += n;
     }
-    ntiles[(int64_t)bh * Cq + a] = acc;
+    nseg[(int64_t)bh * Cq + a] = ns;
+    nkeys[(int64_t)bh * Cq + a] = nk;
   }
   __syncthreads();
-  int2* tl = tiles + ((int64_t)bh * Cq + a) * maxT;
+  int2* sg = segs + ((int64_t)bh * Cq + a) * Ck;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int bb = t + 256 * i;
-    if (bb < Ck && nt[i] > 0) {
-      const int s0 = start_k[sk + bb], s1 = start_k[sk + bb + 1];
-      for (int j = 0; j < nt[i]; ++j) tl[tsc[bb] + j] = make_int2(s0 + j * kBN, min(s1, s0 + (j + 1) * kBN));
-    }
+    if (bb < Ck && nsel[i] > 0) sg[tsc[bb]] = make_int2(start_k[sk + bb], vst[bb]);
   }
-  (void)tot;
 }
 
-// grid (BH): rb_prefix[bh*(Cq+1) + a] = row blocks of 256 before query cluster a.
-__global__ void k_svg2_rows(int32_t Cq, const int32_t* __restrict__ start_q, int32_t* __restrict__ rb_prefix) {
-  const int bh = blockIdx.x;
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  for (int a = 0; a < Cq; ++a) {
-    rb_prefix[(int64_t)bh * (Cq + 1) + a] = acc;
-    const int n = start_q[(int64_t)bh * (Cq + 1) + a + 1] - start_q[(int64_t)bh * (Cq + 1) + a];
-    acc += (n + 255) / 256;
+// grid (BH), 1024 threads: the query clusters of a head in descending work
+// (key tiles of their selection; ties to the lower index; clusters without
+// rows last): ord[bh*Cq + r] = cluster of rank r, rb_prefix[bh*(Cq+1) + r] =
+// row blocks of 256 before rank r (rb_prefix[Cq] = all of the head's).
+__global__ __launch_bounds__(1024) void k_svg2_order(int32_t Cq, const int32_t* __restrict__ start_q,
+                                                     const int32_t* __restrict__ nkeys, int32_t* __restrict__ ord,
+                                                     int32_t* __restrict__ rb_prefix) {
+  __shared__ int work[1024], sc[1024];
+  const int bh = blockIdx.x, a = threadIdx.x;
+  const int64_t sq = (int64_t)bh * (Cq + 1);
+  int nrb = 0, wk = -1;
+  if (a < Cq) {
+    const int n = start_q[sq + a + 1] - start_q[sq + a];
+    nrb = (n + 255) / 256;
+    wk = n > 0 ? (nkeys[(int64_t)bh * Cq + a] + kBN - 1) / kBN : -1;
   }
-  rb_prefix[(int64_t)bh * (Cq + 1) + Cq] = acc;
+  work[a] = wk;
+  __syncthreads();
+  int r = 0;
+  if (a < Cq)
+    for (int o = 0; o < Cq; ++o) r += (work[o] > wk) || (work[o] == wk && o < a);
+  __syncthreads();
+  sc[a] = 0;
+  __syncthreads();
+  if (a < Cq) {
+    ord[(int64_t)bh * Cq + r] = a;
+    sc[r] = nrb;
+  }
+  __syncthreads();
+  const int own = sc[a];
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan over ranks
+    const int v = a >= o ? sc[a - o] : 0;
+    __syncthreads();
+    sc[a] += v;
+    __syncthreads();
+  }
+  if (a < Cq) rb_prefix[sq + a] = sc[a] - own;
+  if (a == Cq - 1) rb_prefix[sq + Cq] = sc[a];
 }
 
 // grid (ceil(L / RPB), BH): dst[bh][i] = src[b, h][perm[bh*L + i]] (rows of D bf16).
@@ -371,39 +469,100 @@ struct Svg2Ptrs {
   const void *q, *kp, *vp;  // q: caller layout; kp, vp: cluster order [BH][L][D]
   svg_strides s, so;
   void* o;
-  const int32_t *perm_q, *start_q, *rb_prefix, *ntiles;
-  const int2* tiles;
-  int32_t Cq, maxT, max_rb;
+  const int32_t *perm_q, *start_q, *ord, *rb_prefix, *nseg, *nkeys;
+  const int2* segs;
+  int32_t Cq, Ck, max_rb, total;
 };
 
+// Direct-to-LDS loads of the key tiles of one query cluster: tile t holds
+// positions 64t .. 64t+63 of the concatenation of the selected key clusters'
+// keys (segments of the cluster-ordered K and V), so only the last tile is
+// ragged (its rows clamp to the last key).  The LDS chunk layout and
+// swizzles are those of the contiguous loader; each lane's row comes from
+// the segment table through a cursor that only moves forward.
+template <int D>
+struct SegLoader {
+  using C = TileCfg<D, 8>;
+  const char* kb;
+  const char* vb;
+  uint32_t colk[C::LOADS], colv[C::LOADS];
+  int rr[C::LOADS], cur[C::LOADS];
+
+  __device__ __forceinline__ void init(const __bf16* K, const __bf16* V, int wave, int lane) {
+    kb = reinterpret_cast<const char*>(K);
+    vb = reinterpret_cast<const char*>(V);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int p = min(i * 8 + wave, C::SEGS - 1) * 64 + lane;
+      const int r = p / C::CR, pos = p % C::CR;
+      rr[i] = r;
+      cur[i] = 0;
+      colk[i] = (uint32_t)((pos ^ C::swz_k(r)) * 16);
+      colv[i] = (uint32_t)((pos ^ C::swz_v(r)) * 16);
+    }
+  }
+
+  __device__ __forceinline__ void load(int t, const int2* sg, int ns, int nk, __bf16* lds_k, __bf16* lds_v, int wave,
+                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int seg = i * 8 + wave;
+      if (C::SEGS % 8 != 0 && seg >= C::SEGS) break;  // wave-uniform
+      const int vpos = min(t * kBN + rr[i], nk - 1);
+      int c = cur[i];
+      while (c + 1 < ns && sg[c + 1].y <= vpos) ++c;
+      cur[i] = c;
+      const int2 e = sg[c];
+      const int64_t row = (int64_t)(e.x + (vpos - e.y)) * (D * 2);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + row + colk[i]), (SVG_LDS void*)(lds_k + seg * 512), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + row + colv[i]), (SVG_LDS void*)(lds_v + seg * 512), 16, 0,
+                                       0);
+    }
+  }
+};
+
+// One workgroup per (head, row block of 256 of a query cluster), the
+// clusters of a head in descending work, XCD-aware: consecutive logical ids
+// run on one XCD, so the row blocks of a cluster share its key tiles in L2.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
   constexpr int WAVES = 8;
   using TC = TileCfg<D, WAVES>;
   extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
   auto lds = reinterpret_cast<__bf16 (*)[2][TC::TILE_ELEMS]>(lds_raw);
+  int2* sg = reinterpret_cast<int2*>(lds_raw + 2 * 2 * TC::TILE_ELEMS);  // [Ck] segment table
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / a.max_rb, j = blockIdx.x % a.max_rb;
+  const int w = blockIdx.x;
+  const int xcd = w & 7, slot = w >> 3;
+  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  if (logical >= a.total) return;
+  const int bh = logical / a.max_rb, j = logical % a.max_rb;
   const int32_t* rbp = a.rb_prefix + (int64_t)bh * (a.Cq + 1);
   if (j >= rbp[a.Cq]) return;
-  int lo_c = 0, hi_c = a.Cq;  // last cluster with rbp[c] <= j
-  while (hi_c - lo_c > 1) {
-    const int mid = (lo_c + hi_c) >> 1;
-    if (rbp[mid] <= j) lo_c = mid; else hi_c = mid;
+  int lo_r = 0, hi_r = a.Cq;  // last rank with rbp[r] <= j
+  while (hi_r - lo_r > 1) {
+    const int mid = (lo_r + hi_r) >> 1;
+    if (rbp[mid] <= j) lo_r = mid; else hi_r = mid;
   }
-  const int cq = lo_c, rb = j - rbp[cq];
+  const int cq = a.ord[(int64_t)bh * a.Cq + lo_r], rb = j - rbp[lo_r];
   const int32_t* stq = a.start_q + (int64_t)bh * (a.Cq + 1);
   const int p0 = stq[cq] + rb * 256, p1 = stq[cq + 1];
   const int b = bh / g.H, h = bh % g.H;
 
-  KVLoader<D, false, WAVES> ld;
+  const int64_t ci = (int64_t)bh * a.Cq + cq;
+  const int ns = a.nseg[ci], nk = a.nkeys[ci];
+  const int2* gsg = a.segs + ci * a.Ck;
+  for (int i = tid; i < ns; i += 64 * WAVES) sg[i] = gsg[i];
+  __syncthreads();
+
+  SegLoader<D> ld;
   const __bf16* kp = static_cast<const __bf16*>(a.kp) + (int64_t)bh * g.L * D;
   const __bf16* vp = static_cast<const __bf16*>(a.vp) + (int64_t)bh * g.L * D;
-  ld.init(kp, vp, D, g.L, wave, lane);
-  const int nt = a.ntiles[(int64_t)bh * a.Cq + cq];
-  const int2* tl = a.tiles + ((int64_t)bh * a.Cq + cq) * a.maxT;
-  if (nt > 0) ld.load(g, tl[0].x, lds[0][0], lds[0][1], wave, lane);
+  ld.init(kp, vp, wave, lane);
+  const int nt = (nk + kBN - 1) / kBN;
+  if (nt > 0) ld.load(0, sg, ns, nk, lds[0][0], lds[0][1], wave, lane);
 
   const int pos = p0 + wave * 32 + (lane & 31);
   const bool valid = pos < p1;
@@ -416,13 +575,12 @@ __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
   wait_vm_all();
   __syncthreads();
   auto step = [&](int t, auto stc) {
-    constexpr int sg = decltype(stc)::value;
-    if (t + 1 < nt) ld.load(g, tl[t + 1].x, lds[sg ^ 1][0], lds[sg ^ 1][1], wave, lane);
+    constexpr int sgi = decltype(stc)::value;
+    if (t + 1 < nt) ld.load(t + 1, sg, ns, nk, lds[sgi ^ 1][0], lds[sgi ^ 1][1], wave, lane);
     if (wave_rows) {
-      const int2 rg = tl[t];
-      const int cnt = rg.y - rg.x;
+      const int cnt = nk - t * kBN;
       f32x16 s0, s1;
-      score_tile<D>(lds[sg][0], qf, lane, s0, s1);
+      score_tile<D>(lds[sgi][0], qf, lane, s0, s1);
       if (cnt < kBN) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -430,7 +588,7 @@ __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
           s1[r] = acc_key(1, r, hh) < cnt ? s1[r] : -INFINITY;
         }
       }
-      st.add_tile(s0, s1, lds[sg][1], lane, g.scale_log2);
+      st.add_tile(s0, s1, lds[sgi][1], lane, g.scale_log2);
     }
     wait_vm_all();
     __syncthreads();
@@ -482,7 +640,10 @@ hipError_t launch_kmeans(const KGeom& g, const void* x, svg_strides s, int32_t C
     hipLaunchKernelGGL(k_km_scan, dim3(BH), dim3(1024), 0, st, g.L, C, nBlk, w.hist, w.base, start);
     hipLaunchKernelGGL(k_km_scatter, dim3((unsigned)nBlk, BH), dim3(256), 0, st, g.L, C, nBlk, labels, w.rank, w.base,
                        perm);
-    hipLaunchKernelGGL(k_km_update, dim3((unsigned)C, BH), dim3((unsigned)g.d), 0, st, g, bx, s, C, perm, start, mu);
+    if (g.d == 64)
+      hipLaunchKernelGGL(k_km_update<64>, dim3((unsigned)C, BH), dim3(256), 0, st, g, bx, s, C, perm, start, mu);
+    else
+      hipLaunchKernelGGL(k_km_update<128>, dim3((unsigned)C, BH), dim3(256), 0, st, g, bx, s, C, perm, start, mu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -496,12 +657,12 @@ hipError_t launch_km_init(const KGeom& g, const void* x, svg_strides s, int32_t 
 }
 
 hipError_t launch_svg2_select(const KGeom& g, int32_t Cq, int32_t Ck, float p, const float* mu_q, const float* mu_k,
-                              const int32_t* start_q, const int32_t* start_k, uint8_t* sel, void* tiles,
-                              int32_t* ntiles, int32_t maxT, int32_t* rb_prefix, hipStream_t st) {
+                              const int32_t* start_q, const int32_t* start_k, uint8_t* sel, void* segs,
+                              int32_t* nseg, int32_t* nkeys, int32_t* ord, int32_t* rb_prefix, hipStream_t st) {
   const unsigned BH = (unsigned)(g.B * g.H);
   hipLaunchKernelGGL(k_svg2_select, dim3((unsigned)Cq, BH), dim3(256), 0, st, g, Cq, Ck, p, mu_q, mu_k, start_k, sel,
-                     static_cast<int2*>(tiles), ntiles, maxT);
-  hipLaunchKernelGGL(k_svg2_rows, dim3(BH), dim3(64), 0, st, Cq, start_q, rb_prefix);
+                     static_cast<int2*>(segs), nseg, nkeys);
+  hipLaunchKernelGGL(k_svg2_order, dim3(BH), dim3(1024), 0, st, Cq, start_q, nkeys, ord, rb_prefix);
   return hipGetLastError();
 }
 
@@ -520,8 +681,8 @@ hipError_t launch_gather_rows(const KGeom& g, const void* src, svg_strides s, co
 }
 
 template <int D, bool OUT_BF16>
-static hipError_t launch_svg2_attn_t(const KGeom& g, const Svg2Ptrs& a, hipStream_t st) {
-  const size_t lds = (size_t)2 * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
+static hipError_t launch_svg2_attn_t(const KGeom& g, const Svg2Ptrs& a, int64_t grid, hipStream_t st) {
+  const size_t lds = (size_t)2 * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16) + (size_t)kSvg2MaxClusters * sizeof(int2);
   auto kern = k_svg2_attn<D, OUT_BF16>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -529,16 +690,14 @@ static hipError_t launch_svg2_attn_t(const KGeom& g, const Svg2Ptrs& a, hipStrea
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t grid = (int64_t)g.B * g.H * a.max_rb;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, g, a);
   return hipGetLastError();
 }
 
 hipError_t launch_svg2_attention(const KGeom& g, const void* q, svg_strides s, const void* kp, const void* vp, void* o,
                                  svg_strides so, bool out_bf16, const int32_t* perm_q, const int32_t* start_q,
-                                 const int32_t* rb_prefix, const void* tiles, const int32_t* ntiles, int32_t Cq,
-                                 int32_t maxT, hipStream_t st) {
+                                 const int32_t* ord, const int32_t* rb_prefix, const void* segs, const int32_t* nseg,
+                                 const int32_t* nkeys, int32_t Cq, int32_t Ck, hipStream_t st) {
   Svg2Ptrs a;
   a.q = q;
   a.kp = kp;
@@ -548,14 +707,22 @@ hipError_t launch_svg2_attention(const KGeom& g, const void* q, svg_strides s, c
   a.o = o;
   a.perm_q = perm_q;
   a.start_q = start_q;
+  a.ord = ord;
   a.rb_prefix = rb_prefix;
-  a.ntiles = ntiles;
-  a.tiles = static_cast<const int2*>(tiles);
+  a.nseg = nseg;
+  a.nkeys = nkeys;
+  a.segs = static_cast<const int2*>(segs);
   a.Cq = Cq;
-  a.maxT = maxT;
-  a.max_rb = (g.L + 255) / 256 + Cq;
-  if (g.d == 64) return out_bf16 ? launch_svg2_attn_t<64, true>(g, a, st) : launch_svg2_attn_t<64, false>(g, a, st);
-  return out_bf16 ? launch_svg2_attn_t<128, true>(g, a, st) : launch_svg2_attn_t<128, false>(g, a, st);
+  a.Ck = Ck;
+  a.max_rb = (g.L + 255) / 256 + Cq;  // sum over clusters of ceil(n_a / 256) is below this
+  const int64_t total = (int64_t)g.B * g.H * a.max_rb;
+  const int64_t per_round = 8 * kXcdRun;
+  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  a.total = (int32_t)total;
+  if (g.d == 64)
+    return out_bf16 ? launch_svg2_attn_t<64, true>(g, a, grid, st) : launch_svg2_attn_t<64, false>(g, a, grid, st);
+  return out_bf16 ? launch_svg2_attn_t<128, true>(g, a, grid, st) : launch_svg2_attn_t<128, false>(g, a, grid, st);
 }
 
 }  // namespace svg

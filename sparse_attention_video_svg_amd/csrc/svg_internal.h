@@ -90,14 +90,14 @@ hipError_t launch_km_init(const KGeom& g, const void* x, svg_strides s, int32_t 
 hipError_t launch_kmeans(const KGeom& g, const void* x, svg_strides s, int32_t C, int32_t iters, float* mu,
                          int32_t* labels, int32_t* perm, int32_t* start, const Svg2Scratch& w, hipStream_t st);
 hipError_t launch_svg2_select(const KGeom& g, int32_t Cq, int32_t Ck, float p, const float* mu_q, const float* mu_k,
-                              const int32_t* start_q, const int32_t* start_k, uint8_t* sel, void* tiles,
-                              int32_t* ntiles, int32_t maxT, int32_t* rb_prefix, hipStream_t st);
+                              const int32_t* start_q, const int32_t* start_k, uint8_t* sel, void* segs,
+                              int32_t* nseg, int32_t* nkeys, int32_t* ord, int32_t* rb_prefix, hipStream_t st);
 hipError_t launch_gather_rows(const KGeom& g, const void* src, svg_strides s, const int32_t* perm, void* dst,
                               hipStream_t st);
 hipError_t launch_svg2_attention(const KGeom& g, const void* q, svg_strides s, const void* kp, const void* vp, void* o,
                                  svg_strides so, bool out_bf16, const int32_t* perm_q, const int32_t* start_q,
-                                 const int32_t* rb_prefix, const void* tiles, const int32_t* ntiles, int32_t Cq,
-                                 int32_t maxT, hipStream_t st);
+                                 const int32_t* ord, const int32_t* rb_prefix, const void* segs, const int32_t* nseg,
+                                 const int32_t* nkeys, int32_t Cq, int32_t Ck, hipStream_t st);
 
 // Sampled-row sweeps (profiling, mode search): per (head, row, key slice)
 // one partial online-softmax state (m in log2 units, l, unnormalised acc) per
