@@ -248,12 +248,8 @@ static hipError_t launch_attn(const KGeom& g, const AttnPtrs& a, int32_t nQT, in
   constexpr int W = kAttnWaves, S = kAttnStages;
   const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   auto kern = k_attn_bf16<D, OUT_BF16, W, S>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, a, nQT, (int32_t)total);
   return hipGetLastError();
 }
@@ -276,12 +272,8 @@ static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, 
   constexpr int S = kAttnStages;
   const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   auto kern = k_prof_sweep<D, VIRT, W, S>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
   const int64_t chunks = (n_rows + 32 * W - 1) / (32 * W);
   const int64_t total = chunks * nsplit * g.B * g.H;
   const int64_t per_round = 8 * kXcdRun;

@@ -374,12 +374,8 @@ static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int6
   constexpr int W = kAttnWaves;
   const size_t lds = 2 * (size_t)Fp8Cfg<D>::TILE_BYTES + 2 * (size_t)TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   auto kern = k_attn_fp8<D, OUT_BF16, W>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, a, nQT, (int32_t)total);
   return hipGetLastError();
 }

@@ -13,17 +13,20 @@
 //    K tiles, argmax of x . mu - 0.5 |mu|^2, ties to the lower index) ->
 //    stable counting sort (k_km_hist: per-block counts and in-block ranks;
 //    k_km_scan: per-cluster totals, starts, per-block bases; k_km_scatter)
-//    -> k_km_update (mean of each cluster's tokens summed in cluster order:
+//    -> k_km_update (mean of each cluster's tokens, fixed-order partial sums:
 //    deterministic).  The last iteration's sort is the permutation.
 //  * k_svg2_select: per query cluster, fp32 centroid scores against every key
 //    cluster, the size-weighted softmax, ranks by comparison, the running sum
-//    in rank order, the top-p prefix, and the tile list of the selected key
-//    clusters (ranges of at most 64 consecutive keys of the cluster order).
+//    in rank order, the top-p prefix, and the segment table of the selected
+//    key clusters (first key in the cluster order, offset in the concatenation
+//    of the selected clusters' keys).  k_svg2_order: per head, the query
+//    clusters in descending work with their row-block prefix sums.
 //  * k_gather_rows: K and V copied into cluster order once.
 //  * k_svg2_attn: one workgroup per (query cluster, block of 256 of its
-//    rows): query rows gathered through the permutation, the tile list swept
-//    with the attention kernel's loader, scores, softmax and P.V (the last
-//    tile of a key cluster masks its missing keys), rows scattered back.
+//    rows): query rows gathered through the permutation, the selected keys
+//    streamed as full 64-key tiles through the segment table (only the last
+//    tile masked), scores, softmax and P.V as in the banded kernel, rows
+//    scattered back.
 #include "attn_common.h"
 
 namespace svg {
@@ -502,8 +505,8 @@ struct SegLoader {
     }
   }
 
-  __device__ __forceinline__ void load(int t, const int2* sg, int ns, int nk, __bf16* lds_k, __bf16* lds_v, int wave,
-                                       int lane) {
+  __device__ __forceinline__ void load(int t, const int2* sg, int ns, int nk, __bf16* lds_k, __bf16* lds_v,
+                                       int wave) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int seg = i * 8 + wave;
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
   const __bf16* vp = static_cast<const __bf16*>(a.vp) + (int64_t)bh * g.L * D;
   ld.init(kp, vp, wave, lane);
   const int nt = (nk + kBN - 1) / kBN;
-  if (nt > 0) ld.load(0, sg, ns, nk, lds[0][0], lds[0][1], wave, lane);
+  if (nt > 0) ld.load(0, sg, ns, nk, lds[0][0], lds[0][1], wave);
 
   const int pos = p0 + wave * 32 + (lane & 31);
   const bool valid = pos < p1;
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
   __syncthreads();
   auto step = [&](int t, auto stc) {
     constexpr int sgi = decltype(stc)::value;
-    if (t + 1 < nt) ld.load(t + 1, sg, ns, nk, lds[sgi ^ 1][0], lds[sgi ^ 1][1], wave, lane);
+    if (t + 1 < nt) ld.load(t + 1, sg, ns, nk, lds[sgi ^ 1][0], lds[sgi ^ 1][1], wave);
     if (wave_rows) {
       const int cnt = nk - t * kBN;
       f32x16 s0, s1;
@@ -684,12 +687,8 @@ template <int D, bool OUT_BF16>
 static hipError_t launch_svg2_attn_t(const KGeom& g, const Svg2Ptrs& a, int64_t grid, hipStream_t st) {
   const size_t lds = (size_t)2 * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16) + (size_t)kSvg2MaxClusters * sizeof(int2);
   auto kern = k_svg2_attn<D, OUT_BF16>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, g, a);
   return hipGetLastError();
 }

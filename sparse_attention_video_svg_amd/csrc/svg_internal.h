@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "svg.h"
+#include <atomic>
 
 namespace svg {
 
@@ -51,6 +52,21 @@ hipError_t launch_build_blocks(const KGeom& g, const int32_t* modes, int32_t BM,
                                int32_t* ranges, int32_t* head_order, hipStream_t st);
 hipError_t launch_permute(const KGeom& g, int elt_bytes, const void* src, svg_strides ss, void* dst,
                           svg_strides ds, const int32_t* modes, int inverse, hipStream_t st);
+
+// Raises a kernel's dynamic-LDS limit on the current device the first time
+// it is launched there.  The attribute is per device, so the caller keeps one
+// flag word per kernel (bit = device id < 64); concurrent first calls just
+// set the attribute twice.
+inline hipError_t ensure_dynamic_lds(const void* kern, size_t bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct AttnPtrs {
   const void *q, *k, *v, *qp, *kp, *vp;
