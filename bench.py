@@ -124,6 +124,13 @@ def cpu_baseline(cfg, inp, labels, d, scale, budget_s=12.0):
     heads = heads[:2]
     rng = np.random.default_rng(99)
     L = c["T"] + c["N"] * c["F"]
+    seen = {}
+
+    def keys_of(mode, r):  # active keys of row r under mode (memoised: rows repeat on small shapes)
+        if (mode, r) not in seen:
+            seen[(mode, r)] = sum(hi - lo for lo, hi in oracle.row_intervals(og, mode, r))
+        return seen[(mode, r)]
+
     flops = 0.0
     elapsed = 0.0
     rows_done = 0
@@ -135,14 +142,39 @@ def cpu_baseline(cfg, inp, labels, d, scale, budget_s=12.0):
             t0 = time.perf_counter()
             oracle.attention_rows(og, int(labels[h]), inp["q"][h], inp["k"][h], inp["v"][h], scale, rows)
             elapsed += time.perf_counter() - t0
+            mode = oracle.TEMPORAL if labels[h] == 1 else int(labels[h])
             for r in rows:
-                iv = oracle.row_intervals(og, oracle.TEMPORAL if labels[h] == 1 else int(labels[h]), int(r))
-                flops += 4.0 * d * sum(hi - lo for lo, hi in iv)
+                flops += 4.0 * d * keys_of(mode, int(r))
             rows_done += m
         n = min(2 * n, 2048)
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows_done} seeded query rows of heads {heads} (labels "
-                      f"{[int(labels[h]) for h in heads]}), fp64 oracle masked attention, {elapsed:.1f} s"}
+    out = {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{rows_done} seeded query rows of heads {heads} (labels "
+                     f"{[int(labels[h]) for h in heads]}), fp64 oracle masked attention, {elapsed:.1f} s",
+           "cpu_model": cpu_model()}
+    if inp["rows"] is not None:
+        # the oracle's profiling of one head on the layer's sampled rows (full,
+        # spatial and temporal attention of those rows), same accounting
+        rows = inp["rows"].astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.profile_head(og, inp["q"][0], inp["k"][0], inp["v"][0], scale, rows)
+        pt = time.perf_counter() - t0
+        pflops = 0.0
+        for mode in (oracle.FULL, oracle.SPATIAL, oracle.TEMPORAL):
+            for r in rows:
+                pflops += 4.0 * d * keys_of(mode, int(r))
+        out["profile_value"] = pflops / pt / 1e12
+        out["profile_sample"] = f"oracle profiling of head 0 on its {rows.size} sampled rows, {pt:.1f} s"
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def search_keys(geom, rows):
@@ -369,6 +401,21 @@ def main():
     prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage.mean(axis=0)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
 
+    # a4 on its own: every head of Q through the layout transformation (one
+    # [B, H, L, d] tensor read and written), timed apart from the step
+    qa = torch.empty_like(q)
+    for _ in range(2):
+        svg.svg_layout_permute(geom, q, qa)
+    pa, pb = ev(), ev()
+    pa.record(stream)
+    for _ in range(5):
+        svg.svg_layout_permute(geom, q, qa)
+    pb.record(stream)
+    torch.cuda.synchronize()
+    perm_all_ms = pa.elapsed_time(pb) / 5
+    perm_all_gbs = 2.0 * q.numel() * q.element_size() / (perm_all_ms * 1e-3) / 1e9
+    del qa
+
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -417,6 +464,9 @@ def main():
         "permute_inv_ms": round(float(inv_ms), 4),
         "permute_fwd_gbs": None if fwd_gbs is None else round(fwd_gbs, 1),
         "permute_inv_gbs": None if inv_gbs is None else round(inv_gbs, 1),
+        "permute_all_heads_ms": round(perm_all_ms, 4),
+        "permute_all_heads_gbs": round(perm_all_gbs, 1),
+        "permute_all_heads_frac_of_hbm": round(perm_all_gbs / 8000.0, 4),
         "effective_flops_per_layer": flops,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
