@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--search", action="store_true", help="also time svg_search_modes on the same inputs")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 E4M3 scores: quantise Q, K (svg_quantize_qk) and run svg_sparse_attention_fp8")
+    ap.add_argument("--fp8-pv", action="store_true",
+                    help="FP8 scores and FP8 P.V: svg_quantize_qk + svg_quantize_v + svg_sparse_attention_fp8_pv")
     ap.add_argument("--svg2", action="store_true",
                     help="also time svg2_forward (SVG2 semantic-aware permutation) on the same geometry")
     ap.add_argument("--svg2-spread", type=float, default=1.0, help="spread of the planted SVG2 group centres")
@@ -334,6 +336,8 @@ def main():
     ranges = torch.empty(H * nQT * 4, dtype=torch.int32, device=dev)
     order = torch.empty(H, dtype=torch.int32, device=dev)
     ws = svg.alloc_workspace(geom, din, n_rows, svg.VIRTUAL_PERMUTE)
+    if args.fp8_pv:
+        args.fp8 = True
     if args.fp8:
         if not bf16:
             sys.exit("--fp8 needs a bf16 workload")
@@ -343,6 +347,9 @@ def main():
         k8 = torch.empty_like(q8)
         sq = torch.empty(H * L, dtype=torch.float32, device=dev)
         sk = torch.empty(H * nkt, dtype=torch.float32, device=dev)
+        if args.fp8_pv:
+            v8 = torch.empty(H * nkt * d * 64, dtype=torch.uint8, device=dev)
+            svh = torch.empty(H, dtype=torch.float32, device=dev)
     flags = svg.VIRTUAL_PERMUTE if args.virtual else 0
     if not args.virtual:
         qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
@@ -366,11 +373,15 @@ def main():
         marks.append(ev()); marks[-1].record(stream)
         if args.fp8:
             svg.svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk)
+            if args.fp8_pv:
+                svg.svg_quantize_v(geom, v, modes, v8, svh)
         elif not args.virtual:
             for s_, d_ in ((q, qp), (k, kp), (v, vp)):
                 svg.svg_layout_permute(geom, s_, d_, modes=modes)
         marks.append(ev()); marks[-1].record(stream)
-        if args.fp8:
+        if args.fp8_pv:
+            svg.svg_sparse_attention_fp8_pv(geom, q8, sq, k8, sk, v8, svh, o, modes, ranges, order)
+        elif args.fp8:
             svg.svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, order)
         else:
             svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op,
@@ -428,7 +439,8 @@ def main():
     flops = 4.0 * d * float(sum(pairs))
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
-    peak = (PEAK_FP8_QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS) if bf16 else PEAK_F32_TFLOPS
+    peak = ((PEAK_FP8_TFLOPS if args.fp8_pv else PEAK_FP8_QK_TFLOPS) if args.fp8 else PEAK_BF16_TFLOPS) \
+        if bf16 else PEAK_F32_TFLOPS
     n_temporal = int((lab == 1).sum())
     elt = 2 if bf16 else 4
     perm_bytes = 2.0 * n_temporal * L * d * elt  # read + write per permuted head-tensor
@@ -452,6 +464,7 @@ def main():
                    "tokens_per_frame": geom.F, "text_tokens": geom.T, "heads": H, "head_dim": d,
                    "a1": geom.a1, "a2": geom.a2, "sampled_rows": n_rows, "layout": "virtual" if args.virtual
                    else "explicit", "scores": "fp8-e4m3 (Q per row, K per 64-key tile)" if args.fp8 else "bf16",
+                   "pv": "fp8-e4m3 (P in-kernel, V per head)" if args.fp8_pv else "bf16",
                    "labels": {"spatial": int((lab == 0).sum()), "temporal": n_temporal,
                                                "full": int((lab == 2).sum()), "other": int((lab > 2).sum())}},
         "attn_ms": round(float(attn_ms), 4),
@@ -471,7 +484,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
                      "traffic": recorded_traffic() if args.config == 2 and not args.virtual and not args.fp8 else None,
-                     "kernel": ("k_attn_fp8 (svg_sparse_attention_fp8)" if args.fp8 else
+                     "kernel": ("k_attn_fp8<PV8> (svg_sparse_attention_fp8_pv)" if args.fp8_pv else
+                                "k_attn_fp8 (svg_sparse_attention_fp8)" if args.fp8 else
                                 "k_attn_bf16 (svg_sparse_attention)") if bf16 else "k_attn_f32"},
     }
     if args.search and bf16:

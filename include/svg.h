@@ -96,6 +96,9 @@ typedef struct {
                                       scores on FP8 E4M3 Q and K, see
                                       svg_quantize_qk; implies the index-map
                                       reads of SVG_FLAG_VIRTUAL_PERMUTE */
+#define SVG_FLAG_FP8_PV 8          /* with SVG_FLAG_FP8_SCORES: P.V on the
+                                      FP8 matrix cores as well (V to E4M3 by
+                                      svg_quantize_v) */
 
 int32_t svg_abi_version(void);
 const char* svg_last_error(void);
@@ -222,6 +225,34 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
                                     svg_strides so, const int32_t* modes, const int32_t* ranges,
                                     const int32_t* head_order, int32_t BM, int32_t BN, void* stream);
 
+/* FP8 P.V, step 1b: V to FP8 E4M3 with one power-of-two scale per head
+ * (Sparse-vDiT review, editorial extensions, as for svg_quantize_qk; the
+ * scheme is ours): s_h = the smallest power of two with 448*s_h >= max|v|
+ * over the head (1 if all zero), codes = E4M3(v / s_h), nearest, ties to
+ * even.  Stored per tile of 64 rows of the head's working layout (as k8),
+ * transposed: v8[((b*H+h)*ceil(L/64) + tile)*d*64 + dim*64 + p] is the code
+ * of row tile*64 + key(p), dim `dim`, where for p = 32*g + j
+ * key(p) = 32*(j/16) + 8*((j%16)/4) + 4*g + j%4 (the order in which the
+ * score accumulators hold their keys); rows beyond L encode 0.
+ * v8: device uint8[B*H*ceil(L/64)*d*64] (16-byte aligned); sv: float[B*H].
+ * bf16 inputs only.  Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED (dtype),
+ * SVG_E_HIP. */
+svg_status svg_quantize_v(const svg_geom* geom, svg_dtype dtype, const void* v, svg_strides s,
+                          const int32_t* modes, uint8_t* v8, float* sv, void* stream);
+
+/* FP8 scores and FP8 P.V, step 2: as svg_sparse_attention_fp8, with the
+ * weights of each row taken as p = 2^(x - m + 6) in E4M3, x the score in
+ * log2 units and m a running reference max that moves when a tile's max
+ * exceeds it by more than 2, so p lies in [2^-9, 2^8] and a key is dropped
+ * only below 2^-15 of the reference; P.V and the row sums both come from the
+ * E4M3 weights (FP8 matrix cores), the output is scaled by sv[b*H+h] once.
+ * Inputs from svg_quantize_qk and svg_quantize_v with the same modes.
+ * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED (tiles), SVG_E_HIP. */
+svg_status svg_sparse_attention_fp8_pv(const svg_geom* geom, svg_dtype out, const uint8_t* q8, const float* sq,
+                                       const uint8_t* k8, const float* sk, const uint8_t* v8, const float* sv,
+                                       void* o, svg_strides so, const int32_t* modes, const int32_t* ranges,
+                                       const int32_t* head_order, int32_t BM, int32_t BN, void* stream);
+
 /* SVG2: semantic-aware permutation ("Sparse VideoGen2 ..." explainer,
  * 2. Methodology, A-C).  Q and K rows of each head are clustered
  * independently by k-means into C_q / C_k clusters (Lloyd: `iters`
@@ -271,7 +302,9 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* params, svg_dty
 
 /* One attention layer of the method, as a diffusion step runs it:
  * (with SVG_FLAG_FP8_SCORES the attention is svg_quantize_qk followed by
- * svg_sparse_attention_fp8 and no permuted copies are made)
+ * svg_sparse_attention_fp8 and no permuted copies are made; with
+ * SVG_FLAG_FP8_PV as well, svg_quantize_qk, svg_quantize_v and
+ * svg_sparse_attention_fp8_pv)
  *   modes_in == NULL: profile on `rows` (writes labels_out, stats_out), else
  *   use modes_in (Sparse-vDiT's fixed per-head modes; no profiling, rows and
  *   stats_out unused, labels_out receives a copy of modes_in);

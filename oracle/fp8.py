@@ -15,7 +15,13 @@ scheme is therefore a reading, stated here and in the design notes:
   - Q: one scale per token row; K: one scale per tile of 64 rows of the
     head's working layout (token-major for TEMPORAL heads); the scale is the
     smallest power of two s with 448 * s >= max |x| (s = 1 for an all-zero
-    group), so every scaled value lies in [-448, 448].
+    group), so every scaled value lies in [-448, 448];
+  - with FP8 P.V as well: V with one scale per head (the same rule over the
+    whole head), and the attention weights in E4M3.  The weights' rounding
+    depends on the kernel's running reference max, so no plain oracle
+    reproduces it; the oracle for that mode is the exact softmax on the
+    dequantised Q, K, V, and the tests bound the weights' rounding
+    analytically from the oracle's own weights.
 """
 import numpy as np
 
@@ -89,3 +95,10 @@ def dequant_rows(codes, s):
 def dequant_tiles(codes, s, tile=KEY_TILE):
     L = codes.shape[0]
     return e4m3_decode(codes) * np.repeat(np.asarray(s), tile)[:L, None]
+
+
+def quantize_head(x):
+    """One scale for a whole [L, d] group: (codes uint8 [L, d], scale)."""
+    x = np.asarray(x, dtype=np.float64)
+    s = pow2_scale(np.max(np.abs(x)) if x.size else 0.0)
+    return e4m3_encode(x / s), s

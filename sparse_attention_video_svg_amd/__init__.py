@@ -18,7 +18,8 @@ __all__ = [
     "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE", "MODE_SEARCH",
     "FP8_SCORES", "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
     "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
-    "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_layer_forward", "library_path",
+    "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_quantize_v",
+    "svg_sparse_attention_fp8_pv", "FP8_PV", "svg_layer_forward", "library_path",
     "Svg2Params", "SVG2_INIT_GIVEN", "svg2_workspace_bytes", "svg2_kmeans", "svg2_forward",
 ]
 
@@ -27,6 +28,7 @@ F32, BF16 = 0, 1
 VIRTUAL_PERMUTE = 1
 MODE_SEARCH = 2  # svg_workspace_bytes: size for svg_search_modes
 FP8_SCORES = 4   # svg_layer_forward: scores on FP8 E4M3 Q and K
+FP8_PV = 8       # with FP8_SCORES: P.V on FP8 E4M3 weights and V as well
 SEARCH_CANDIDATES = (SKIP, WINDOW, TEMPORAL, STRIPE)  # order of svg_search_modes' stats
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -149,6 +151,8 @@ def _lib():
                                       i32, vp], i32),
             "svg_quantize_qk": ([g, i32, vp, vp, S, vp, vp, vp, vp, vp, vp], i32),
             "svg_sparse_attention_fp8": ([g, i32, vp, vp, vp, vp, vp, S, vp, S, vp, vp, vp, i32, i32, vp], i32),
+            "svg_quantize_v": ([g, i32, vp, S, vp, vp, vp, vp], i32),
+            "svg_sparse_attention_fp8_pv": ([g, i32, vp, vp, vp, vp, vp, vp, vp, S, vp, vp, vp, i32, i32, vp], i32),
             "svg2_workspace_bytes": ([g, P(_Svg2Params), P(ctypes.c_size_t)], i32),
             "svg2_kmeans": ([g, i32, vp, S, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
             "svg2_forward": ([g, P(_Svg2Params), i32, i32, vp, vp, vp, S, vp, S, i32, vp, vp, vp, vp,
@@ -304,6 +308,25 @@ def svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, head_ord
     _check(_lib().svg_sparse_attention_fp8(ctypes.byref(g), _dtype_code(o), _ptr(q8), _ptr(sq), _ptr(k8), _ptr(sk),
                                            _ptr(v), _strides(v), _ptr(o), _strides(o), _ptr(modes), _ptr(ranges),
                                            _ptr(head_order), BM, BN, _stream(stream)))
+
+
+def svg_quantize_v(geom, v, modes, v8, sv, stream=None):
+    """FP8 E4M3 quantisation of V with one scale per head, stored per 64-key
+    tile of the working layout, transposed: v8 uint8 [B*H*ceil(L/64)*d*64];
+    sv float32 [B*H]."""
+    _check_shape(geom, v, "v")
+    g = geom.c()
+    _check(_lib().svg_quantize_v(ctypes.byref(g), _dtype_code(v), _ptr(v), _strides(v), _ptr(modes), _ptr(v8),
+                                 _ptr(sv), _stream(stream)))
+
+
+def svg_sparse_attention_fp8_pv(geom, q8, sq, k8, sk, v8, sv, o, modes, ranges, head_order, stream=None):
+    _check_shape(geom, o, "o")
+    BM, BN = svg_tile_config(BF16, geom.d)
+    g = geom.c()
+    _check(_lib().svg_sparse_attention_fp8_pv(ctypes.byref(g), _dtype_code(o), _ptr(q8), _ptr(sq), _ptr(k8),
+                                              _ptr(sk), _ptr(v8), _ptr(sv), _ptr(o), _strides(o), _ptr(modes),
+                                              _ptr(ranges), _ptr(head_order), BM, BN, _stream(stream)))
 
 
 def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_out=None, modes_in=None,

@@ -146,6 +146,12 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
     off = align256(off + sizeof(float) * (size_t)BH * g.L);
     w.sk = off;
     off = align256(off + sizeof(float) * (size_t)BH * nKT);
+    if (flags & SVG_FLAG_FP8_PV) {
+      w.v8 = off;
+      off = align256(off + (size_t)BH * nKT * g.d * 64);
+      w.svh = off;
+      off = align256(off + sizeof(float) * (size_t)BH);
+    }
   } else if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
     // token-major Q, K, V in the input dtype, then O sized for fp32 output
     w.perm_tensor_bytes = align256((size_t)BH * g.L * g.d * elt_bytes(dtype));
@@ -373,8 +379,10 @@ svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_
   if (!bytes) return fail(SVG_E_INVALID, "bytes is NULL");
   if (n_rows < 0 || (int64_t)n_rows > (int64_t)g.N * g.F)
     return fail(SVG_E_INVALID, "n_rows=%d must be in [0, N*F]", n_rows);
-  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH | SVG_FLAG_FP8_SCORES))
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_MODE_SEARCH | SVG_FLAG_FP8_SCORES | SVG_FLAG_FP8_PV))
     return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & SVG_FLAG_FP8_PV) && !(flags & SVG_FLAG_FP8_SCORES))
+    return fail(SVG_E_INVALID, "SVG_FLAG_FP8_PV needs SVG_FLAG_FP8_SCORES");
   if ((flags & (SVG_FLAG_MODE_SEARCH | SVG_FLAG_FP8_SCORES)) && dtype != SVG_BF16)
     return fail(SVG_E_UNSUPPORTED, "the mode search and fp8 scores take bf16 inputs");
   *bytes = ws_layout(g, dtype, n_rows, flags).total;
@@ -517,6 +525,46 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8");
 }
 
+svg_status svg_quantize_v(const svg_geom* geom, svg_dtype dtype, const void* v, svg_strides s, const int32_t* modes,
+                          uint8_t* v8, float* sv, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (dtype != SVG_BF16) return fail(dtype_ok(dtype) ? SVG_E_UNSUPPORTED : SVG_E_INVALID, "fp8 V takes bf16 inputs");
+  TRY(check_ptr(v, "v", 16));
+  TRY(check_strides(s, g, 2, "v"));
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(v8, "v8", 16));
+  TRY(check_ptr(sv, "sv", 4));
+  hipError_t e = launch_quant_v(g, v, s, modes, v8, sv, (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_quantize_v");
+}
+
+svg_status svg_sparse_attention_fp8_pv(const svg_geom* geom, svg_dtype out, const uint8_t* q8, const float* sq,
+                                       const uint8_t* k8, const float* sk, const uint8_t* v8, const float* sv,
+                                       void* o, svg_strides so, const int32_t* modes, const int32_t* ranges,
+                                       const int32_t* head_order, int32_t BM, int32_t BN, void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
+  if (BM != kBM_bf16 || BN != kBN_bf16)
+    return fail(SVG_E_UNSUPPORTED, "ranges built with %dx%d tiles; this kernel needs %dx%d", BM, BN, kBM_bf16,
+                kBN_bf16);
+  TRY(check_ptr(q8, "q8", 16));
+  TRY(check_ptr(k8, "k8", 16));
+  TRY(check_ptr(sq, "sq", 4));
+  TRY(check_ptr(sk, "sk", 4));
+  TRY(check_ptr(v8, "v8", 16));
+  TRY(check_ptr(sv, "sv", 4));
+  TRY(check_ptr(o, "o", 16));
+  TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_ptr(modes, "modes", 4));
+  TRY(check_ptr(ranges, "ranges", 16));
+  TRY(check_ptr(head_order, "head_order", 4));
+  hipError_t e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8_pv");
+}
+
 svg_status svg2_workspace_bytes(const svg_geom* geom, const svg2_params* prm, size_t* bytes) {
   KGeom g;
   TRY(check_geom(geom, &g));
@@ -607,9 +655,12 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
   KGeom g;
   TRY(check_geom(geom, &g));
   if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
-  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_FP8_SCORES))
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_FP8_SCORES | SVG_FLAG_FP8_PV))
     return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & SVG_FLAG_FP8_PV) && !(flags & SVG_FLAG_FP8_SCORES))
+    return fail(SVG_E_INVALID, "SVG_FLAG_FP8_PV needs SVG_FLAG_FP8_SCORES");
   const bool fp8 = flags & SVG_FLAG_FP8_SCORES;
+  const bool fp8pv = flags & SVG_FLAG_FP8_PV;
   if (fp8 && in != SVG_BF16) return fail(SVG_E_UNSUPPORTED, "fp8 scores take bf16 inputs");
   if (fp8) flags |= SVG_FLAG_VIRTUAL_PERMUTE;  // the fp8 path reads temporal heads through the index map
   const bool profile = modes_in == nullptr;
@@ -656,6 +707,14 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
     float* sk = ws_at<float>(ws, w.sk);
     e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, st);
     if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 quantisation)");
+    if (fp8pv) {
+      uint8_t* v8 = ws_at<uint8_t>(ws, w.v8);
+      float* svh = ws_at<float>(ws, w.svh);
+      e = launch_quant_v(g, v, s, modes, v8, svh, st);
+      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 V quantisation)");
+      e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, svh, o, so, out == SVG_BF16, modes, ranges, order, st);
+      return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
+    }
     e = launch_attention_fp8(g, q8, sq, k8, sk, v, s, o, so, out == SVG_BF16, modes, ranges, order, st);
     return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
   }

@@ -43,6 +43,7 @@ struct WsLayout {
   size_t part_acc, part_ml, row_sums, ord_x, ord_r;  // profiling
   size_t labels, ranges, order, perm, total;
   size_t q8, k8, sq, sk;     // fp8-score path: quantised Q, K and their scales
+  size_t v8, svh;            // fp8 P.V: quantised V tiles and per-head scales
   size_t perm_tensor_bytes;  // one permuted tensor (all heads)
   int32_t ksplit;            // key splits of the profiling sweep
 };
@@ -89,6 +90,16 @@ hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const float* 
                                 const float* sk, const void* v, svg_strides sv, void* o, svg_strides so,
                                 bool out_bf16, const int32_t* modes, const int32_t* ranges, const int32_t* order,
                                 hipStream_t st);
+// FP8 P.V: V to E4M3 with one power-of-two scale per head, stored per 64-key
+// tile of the working layout, transposed (v8: [B*H, ceil(L/64), d, 64]
+// bytes in P-register key order; svh: [B*H] scales), and the attention kernel
+// that takes Q8/K8 and V8 (scores and P.V on the FP8 matrix cores).
+hipError_t launch_quant_v(const KGeom& g, const void* v, svg_strides s, const int32_t* modes, uint8_t* v8,
+                          float* svh, hipStream_t st);
+hipError_t launch_attention_fp8pv(const KGeom& g, const uint8_t* q8, const float* sq, const uint8_t* k8,
+                                  const float* sk, const uint8_t* v8, const float* svh, void* o, svg_strides so,
+                                  bool out_bf16, const int32_t* modes, const int32_t* ranges, const int32_t* order,
+                                  hipStream_t st);
 
 // SVG2 (semantic-aware permutation): k-means of one tensor per head
 // (`iters` Lloyd iterations from the centroids in mu, which are updated in

@@ -243,3 +243,29 @@ def test_svg2_validation():
     assert km(mu=None) == E_INVALID and km(lab=None) == E_INVALID
     assert km(perm=None) == E_INVALID and km(start=None) == E_INVALID
     assert km(wsb=16) == E_WORKSPACE
+
+
+def test_fp8_pv_validation():
+    g = geom().c()
+    L = raw()
+    s = strides()
+    assert L.svg_quantize_v(ctypes.byref(g), svg.F32, A, s, A, A, A, None) == E_UNSUPPORTED
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, A, None, A, None) == E_INVALID
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, A, A, None, None) == E_INVALID
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, None, A, A, None) == E_INVALID
+
+    def att(BM=BM_BF16, BN=BN_BF16, v8=A, sv=A, out=svg.BF16):
+        return L.svg_sparse_attention_fp8_pv(ctypes.byref(g), out, A, A, A, A, v8, sv, A, s, A, A, A, BM, BN, None)
+
+    assert att(BM=BM_BF16 // 2) == E_UNSUPPORTED
+    assert att(v8=None) == E_INVALID
+    assert att(sv=None) == E_INVALID
+    assert att(out=9) == E_INVALID
+    gg = geom()
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.FP8_PV)
+    assert e.value.status == E_INVALID
+    a = svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.FP8_SCORES)
+    b = svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.FP8_SCORES | svg.FP8_PV)
+    nkt = -(-gg.L // 64)
+    assert b - a >= gg.H * nkt * gg.d * 64

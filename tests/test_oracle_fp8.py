@@ -90,3 +90,44 @@ def test_representable_values_are_unchanged():
     c, s = fp8.quantize_rows(x)
     assert np.all(s == 2.0 ** -3) and np.array_equal(c, codes)
     assert np.array_equal(fp8.dequant_rows(c, s), x)
+
+
+def test_quantize_head():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 1.5, (200, 64)).astype(np.float32).astype(np.float64)
+    c, s = fp8.quantize_head(x)
+    assert c.shape == x.shape and c.dtype == np.uint8
+    assert 224.0 < np.max(np.abs(x)) / s <= 448.0 and np.log2(s) == np.round(np.log2(s))
+    d = fp8.e4m3_decode(c) * s
+    assert np.all(np.abs(d - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s))
+    z, sz = fp8.quantize_head(np.zeros((5, 8)))
+    assert sz == 1.0 and np.all(z == 0)
+    # values that are E4M3 numbers times the head's scale come back exactly
+    codes = rng.integers(0, 0x7F, (40, 16)).astype(np.uint8)
+    codes[3, 3] = 0x7E
+    y = fp8.e4m3_decode(codes) * 2.0 ** -5
+    cy, sy = fp8.quantize_head(y)
+    assert sy == 2.0 ** -5 and np.array_equal(cy, codes)
+
+
+@pytest.mark.parametrize("spread,n,seed", [(0.5, 300, 0), (4.0, 300, 1), (20.0, 500, 2), (0.05, 4000, 3),
+                                           (30.0, 6000, 4)])
+def test_fp8_weight_bound_holds_for_emulated_rounding(spread, n, seed):
+    """The bound used for the FP8 P.V outputs, checked against the scheme
+    emulated here: weights 2^(x - m_ref + 6) rounded to E4M3 by the oracle's
+    encoder for references m_ref anywhere in [m - 2, m], with flat rows
+    (many keys far below the max) and peaky ones."""
+    from fp8_bounds import fp8_pv_bound
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, spread, n)
+    x[rng.integers(0, n)] += 3 * spread  # one dominant key
+    v = rng.normal(0, 1, (n, 16))
+    m = x.max()
+    w = np.exp2(x - m)
+    w /= w.sum()
+    o = w @ v
+    bound = fp8_pv_bound(x, w, v, o)
+    for m_ref in (m, m - 0.5, m - 1.3, m - 2.0):
+        p = fp8.e4m3_decode(fp8.e4m3_encode(np.exp2(x - m_ref + 6)))
+        o8 = (p @ v) / p.sum()
+        assert np.all(np.abs(o8 - o) <= bound + 1e-12), (m_ref, np.max(np.abs(o8 - o) - bound))
