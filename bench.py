@@ -285,7 +285,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", "--config", dest="config", type=int, default=2,
+                    help="synthetic workload: 0 tiny fp32 4x64, 1 CogVideoX-shaped 13x4080 h48 d64, "
+                         "2 HunyuanVideo-shaped 33x3600 h24 d128 (default), 3 the same with 256 text tokens and "
+                         "mixed heads, 4 Sparse-vDiT pattern set 21x1560 h40 d128")
     ap.add_argument("--call", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--virtual", action="store_true",
@@ -302,7 +305,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by head with no "
-              "cross-GPU exchange, and multi-GPU runs are not part of this build.", file=sys.stderr)
+              "cross-GPU exchange, and multi-GPU measurement is not implemented here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -311,11 +314,11 @@ def main():
     import sparse_attention_video_svg_amd as svg
     import svg_synth as S
 
-    cfg = S.CONFIGS[args.config]
+    cfg = S.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     t0 = time.time()
     inp = S.make_inputs(args.config, call=args.call)
-    log(f"inputs for config {args.config} generated in {time.time() - t0:.1f} s")
+    log(f"inputs for workload {args.config} ({cfg['name']}) generated in {time.time() - t0:.1f} s")
     bf16 = cfg["dtype"] == "bf16"
     tdt = torch.bfloat16 if bf16 else torch.float32
     din = svg.BF16 if bf16 else svg.F32
@@ -460,7 +463,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded planted Q/K/V, no model activations)",
-        "config": {"workload": f"{cfg['name']} (config {args.config})", "frames": geom.N,
+        "config": {"workload": cfg["name"], "frames": geom.N,
                    "tokens_per_frame": geom.F, "text_tokens": geom.T, "heads": H, "head_dim": d,
                    "a1": geom.a1, "a2": geom.a2, "sampled_rows": n_rows, "layout": "virtual" if args.virtual
                    else "explicit", "scores": "fp8-e4m3 (Q per row, K per 64-key tile)" if args.fp8 else "bf16",

@@ -27,7 +27,9 @@ import numpy as np
 SPATIAL, TEMPORAL, FULL, SKIP, WINDOW, STRIPE = range(6)
 UNSTRUCTURED = FULL  # an unstructured head carries no planted signal
 
-CONFIGS = {
+# the synthetic workloads (shapes of the pages' models), by index and name
+TINY_FP32, COGVIDEOX, HUNYUANVIDEO, HUNYUANVIDEO_TEXT, SPARSE_VDIT = range(5)
+WORKLOADS = {
     0: dict(name="tiny-fp32 4x64 h2 d64", N=4, F=64, T=0, H=2, d=64, a1=1, a2=8, dtype="f32",
             signal=3.0, noise=0.3, sample="all"),
     1: dict(name="cogvideox-like 13x4080 h48 d64", N=13, F=4080, T=0, H=48, d=64, a1=2, a2=170,
@@ -64,7 +66,7 @@ def sample_rows(N, F, T, frac, seed):
 
 
 def head_kinds(cfg, rng):
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     H = c["H"]
     if cfg == 0:
         return np.array([SPATIAL, TEMPORAL], dtype=np.int32)
@@ -129,7 +131,7 @@ def make_inputs(cfg, call=0, heads=None, workers=8):
     head has its own random stream, so a subset is drawn identically).
     """
     import concurrent.futures
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     N, F, T, H, d = c["N"], c["F"], c["T"], c["H"], c["d"]
     L = T + N * F
     seed = 1000 * cfg + call

@@ -62,8 +62,8 @@ CASES = [(0, 0), (1, 0), (2, 0), (3, 0), (3, 1), (3, 2), (3, 3), (4, 0)]
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg,call", CASES)
 def test_layer_parity(cfg, call):
-    c = S.CONFIGS[cfg]
-    print(f"\n[config {cfg} call {call}: {c['name']}]", flush=True)
+    c = S.WORKLOADS[cfg]
+    print(f"\n[workload {cfg} call {call}: {c['name']}]", flush=True)
     inp = S.make_inputs(cfg, call=call)
     g = geom_of(c)
     bf16 = c["dtype"] == "bf16"

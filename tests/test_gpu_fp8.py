@@ -106,9 +106,9 @@ def test_fp8_layer_hunyuanvideo_shape():
     """The whole layer with fp8 scores on the HunyuanVideo-shaped workload
     (profiling, tile lists, quantisation, attention): labels as the planted
     types, sampled rows of two heads against the oracle on dequantised Q, K."""
-    c = S.CONFIGS[2]
+    c = S.WORKLOADS[S.HUNYUANVIDEO]
     heads = [0, 1]
-    inp = S.make_inputs(2, call=0)
+    inp = S.make_inputs(S.HUNYUANVIDEO, call=0)
     g = svg.Geom(B=1, H=c["H"], d=c["d"], N=c["N"], F=c["F"], T=c["T"], a1=c["a1"], a2=c["a2"], window=c["F"],
                  stripe=512)
     q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
@@ -245,8 +245,8 @@ def test_fp8_pv_layer_hunyuanvideo_shape():
     """The whole layer with FP8 scores and FP8 P.V on the HunyuanVideo-shaped
     workload: labels as the planted types, sampled rows of two heads within
     the E4M3-weight bound of the oracle on dequantised Q, K, V."""
-    c = S.CONFIGS[2]
-    inp = S.make_inputs(2, call=0)
+    c = S.WORKLOADS[S.HUNYUANVIDEO]
+    inp = S.make_inputs(S.HUNYUANVIDEO, call=0)
     g = svg.Geom(B=1, H=c["H"], d=c["d"], N=c["N"], F=c["F"], T=c["T"], a1=c["a1"], a2=c["a2"], window=c["F"],
                  stripe=512)
     q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")

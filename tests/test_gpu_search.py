@@ -82,8 +82,8 @@ def test_search_sparse_vdit_shape(lam):
     8 heads per planted kind), 1 % of the video rows sampled; the oracle
     checks 2 heads of each kind, the planted window / temporal / stripe heads
     must pick their own mode when the penalty is small."""
-    c = S.CONFIGS[4]
-    inp = S.make_inputs(4, call=0)
+    c = S.WORKLOADS[S.SPARSE_VDIT]
+    inp = S.make_inputs(S.SPARSE_VDIT, call=0)
     g = svg.Geom(B=1, H=c["H"], d=c["d"], N=c["N"], F=c["F"], T=c["T"], a1=c["a1"], a2=c["a2"],
                  window=c["window"], stripe=c["stripe"])
     rows_np = S.sample_rows(c["N"], c["F"], c["T"], 0.01, 4500)
