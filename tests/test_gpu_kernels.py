@@ -179,3 +179,57 @@ def test_profile_labels_bit_exact(dt, N, F, T, d, a1, a2):
         assert lab[h] == want, (h, lab[h], want, st[h], ref)
         # statistics: relative errors to 2 % (absolute floor 1e-4 for near-zero errors)
         np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
+
+
+LAYOUT_CASES = [
+    # B, H, N, F, T, d, a1, a2, window, stripe, modes (B*H of them)
+    (2, 3, 4, 50, 5, 128, 1, 6, 40, 60, [svg.SPATIAL, svg.TEMPORAL, svg.FULL, svg.WINDOW, svg.STRIPE, svg.SKIP]),
+    (1, 2, 1, 200, 0, 64, 1, 30, 50, 64, [svg.SPATIAL, svg.TEMPORAL]),              # one frame
+    (1, 2, 150, 1, 3, 128, 4, 1, 9, 20, [svg.SPATIAL, svg.TEMPORAL]),               # one token per frame
+    (1, 3, 1, 7, 2, 64, 1, 2, 3, 4, [svg.SPATIAL, svg.TEMPORAL, svg.FULL]),         # shorter than a tile
+    (2, 2, 5, 30, 4, 128, 5, 30, 200, 500, [svg.SPATIAL, svg.TEMPORAL, svg.WINDOW, svg.STRIPE]),  # bands wider
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES)
+@pytest.mark.parametrize("virtual", [False, True])
+def test_attention_strided_batched_and_degenerate(case, virtual):
+    """B = 2 with Q, K, V, O as [B, L, H, d] memory viewed as [B, H, L, d]
+    (token-interleaved heads), and degenerate geometries: a single frame, one
+    token per frame, fewer tokens than one tile, bands wider than the video."""
+    B, H, N, F, T, d, a1, a2, W, St, modes = case
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2, window=W, stripe=St)
+    L = g.L
+    kinds = [planted_kind(m) for m in modes]
+    inp = S.small_config(N, F, T, B * H, d, a1, a2, kinds, seed=B * 100 + N + F, window=W, stripe=St)
+    print(f"\n[strided/degenerate B={B} H={H} N={N} F={F} T={T} d={d} virtual={virtual}]", flush=True)
+
+    def interleaved(a, dtype):  # [B*H, L, d] -> [B, L, H, d] memory, viewed [B, H, L, d]
+        t = torch.from_numpy(np.ascontiguousarray(a.reshape(B, H, L, d).transpose(0, 2, 1, 3))).to(dtype).cuda()
+        return t.permute(0, 2, 1, 3)
+
+    q, k, v = (interleaved(inp[n], torch.bfloat16) for n in "qkv")
+    assert q.stride() == (L * H * d, d, H * d, 1)
+    BM, BN = svg.svg_tile_config(svg.BF16, d)
+    nq = -(-L // BM)
+    modes_t = torch.tensor(modes, dtype=torch.int32, device="cuda")
+    ranges = torch.empty(B * H * nq * 4, dtype=torch.int32, device="cuda")
+    order = torch.empty(B * H, dtype=torch.int32, device="cuda")
+    svg.svg_build_blocks(g, modes_t, BM, BN, ranges, order)
+    o = interleaved(np.full((B * H, L, d), np.nan, dtype=np.float32), torch.bfloat16)
+    if virtual:
+        svg.svg_sparse_attention(g, q, k, v, o, modes_t, ranges, order, flags=svg.VIRTUAL_PERMUTE)
+    else:
+        qp, kp, vp = (torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+        for s_, d_ in ((q, qp), (k, kp), (v, vp)):
+            svg.svg_layout_permute(g, s_, d_, modes=modes_t)
+        op = torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda")
+        svg.svg_sparse_attention(g, q, k, v, o, modes_t, ranges, order, qp=qp, kp=kp, vp=vp, op=op)
+        svg.svg_layout_permute(g, op, o, modes=modes_t, inverse=True)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy().reshape(B * H, L, d)
+    og = ogeom(g)
+    rows = np.arange(L)
+    for bh, mode in enumerate(modes):
+        ref = oracle.attention_rows(og, mode, inp["q"][bh], inp["k"][bh], inp["v"][bh], scale_of(g), rows)
+        check_close(got[bh], ref, "bf16", what=f"head {bh} mode {mode}")
