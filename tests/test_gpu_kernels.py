@@ -233,3 +233,32 @@ def test_attention_strided_batched_and_degenerate(case, virtual):
     for bh, mode in enumerate(modes):
         ref = oracle.attention_rows(og, mode, inp["q"][bh], inp["k"][bh], inp["v"][bh], scale_of(g), rows)
         check_close(got[bh], ref, "bf16", what=f"head {bh} mode {mode}")
+
+
+@pytest.mark.parametrize("n_rows_frac,seed", [(None, 1), (0.2, 2)])
+def test_profile_strided_batched(n_rows_frac, seed):
+    """Profiling with B = 2 on token-interleaved [B, L, H, d] memory, once with a
+    single sampled row (the smallest sample) and once with 20 % of the rows:
+    labels bit-exact, statistics as in the contiguous test."""
+    B, H, N, F, T, d, a1, a2 = 2, 3, 5, 60, 6, 128, 2, 9
+    kinds = [S.SPATIAL, S.TEMPORAL, S.UNSTRUCTURED, S.TEMPORAL, S.SPATIAL, S.SPATIAL]
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2)
+    L = g.L
+    inp = S.small_config(N, F, T, B * H, d, a1, a2, kinds, seed=40 + seed)
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n].reshape(B, H, L, d).transpose(0, 2, 1, 3)))
+         .to(torch.bfloat16).cuda().permute(0, 2, 1, 3) for n in "qkv"}
+    rows_np = np.array([T + 77], dtype=np.int32) if n_rows_frac is None else S.sample_rows(N, F, T, n_rows_frac, seed)
+    rows = torch.from_numpy(rows_np).cuda()
+    labels = torch.empty(B * H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(B * H * 3, dtype=torch.float32, device="cuda")
+    ws = svg.alloc_workspace(g, svg.BF16, rows.numel(), svg.VIRTUAL_PERMUTE)
+    print(f"\n[profile strided B={B} rows={rows_np.size}]", flush=True)
+    svg.svg_profile_heads(g, t["q"], t["k"], t["v"], rows, labels, stats, ws)
+    torch.cuda.synchronize()
+    lab = labels.cpu().numpy()
+    st = stats.cpu().numpy().reshape(B * H, 3)
+    og = ogeom(g)
+    for bh in range(B * H):
+        want, ref = oracle.profile_head(og, inp["q"][bh], inp["k"][bh], inp["v"][bh], scale_of(g), rows_np)
+        assert lab[bh] == want, (bh, lab[bh], want, st[bh], ref)
+        np.testing.assert_allclose(st[bh], ref, rtol=2e-2, atol=1e-4)
