@@ -272,3 +272,39 @@ def test_fp8_pv_layer_hunyuanvideo_shape():
         worst = check_fp8_pv_rows(got[h][check_rows], qd, kd, vd, og, int(lab[h]), scale_of(g), check_rows,
                                   f"fp8 P.V layer head {h}")
         print(f"  head {h} (label {lab[h]}): worst err / bound {worst:.3f}", flush=True)
+
+
+def test_fp8_strided_equals_contiguous():
+    """Token-interleaved [B, L, H, d] inputs (B = 2): Q8, K8, V8 codes, scales
+    and both FP8 attention outputs bit-identical to the contiguous run."""
+    B, H, N, F, T, d = 2, 3, 4, 70, 6, 128
+    modes = [svg.SPATIAL, svg.TEMPORAL, svg.FULL, svg.WINDOW, svg.STRIPE, svg.TEMPORAL]
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T, a1=2, a2=8, window=50, stripe=64)
+    L = g.L
+    inp = S.small_config(N, F, T, B * H, d, 2, 8, [PLANT[m] for m in modes], seed=31, window=50, stripe=64)
+    modes_t = torch.tensor(modes, dtype=torch.int32, device="cuda")
+    BM, BN = svg.svg_tile_config(svg.BF16, d)
+    nq = -(-L // BM)
+    ranges = torch.empty(B * H * nq * 4, dtype=torch.int32, device="cuda")
+    order = torch.empty(B * H, dtype=torch.int32, device="cuda")
+    svg.svg_build_blocks(g, modes_t, BM, BN, ranges, order)
+    print("\n[fp8 strided vs contiguous]", flush=True)
+    res = []
+    for interleave in (False, True):
+        if interleave:
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[n].reshape(B, H, L, d).transpose(0, 2, 1, 3)))
+                       .to(torch.bfloat16).cuda().permute(0, 2, 1, 3) for n in "qkv")
+            mk_o = lambda: torch.full((B, L, H, d), float("nan"), dtype=torch.bfloat16,
+                                      device="cuda").permute(0, 2, 1, 3)
+        else:
+            q, k, v = (to_device(inp[n].reshape(B, H, L, d), torch.bfloat16) for n in "qkv")
+            mk_o = lambda: torch.full((B, H, L, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        q8, sq, k8, sk = quantize_on_gpu(g, q, k, modes_t)
+        v8, sv = quantize_v_on_gpu(g, v, modes_t)
+        o1, o2 = mk_o(), mk_o()
+        svg.svg_sparse_attention_fp8(g, q8, sq, k8, sk, v, o1, modes_t, ranges, order)
+        svg.svg_sparse_attention_fp8_pv(g, q8, sq, k8, sk, v8, sv, o2, modes_t, ranges, order)
+        torch.cuda.synchronize()
+        res.append([t.float().cpu().numpy() for t in (q8, sq, k8, sk, v8, sv, o1, o2)])
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
