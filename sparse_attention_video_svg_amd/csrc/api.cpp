@@ -94,17 +94,30 @@ svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const ch
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
-  // key slices of each profiling sweep: enough workgroups (rows chunk x
-  // head x slice) to give every CU about four
+  // key slices of each profiling sweep.  The full sweep runs one workgroup
+  // (rows chunk x head x slice) per CU at a time, so its time goes as
+  // ceil(workgroups / CUs) rounds of 1/ks of a chunk's keys each: take the
+  // ks in 1..16 (and at most the key tiles) that minimises rounds / ks; on
+  // ties the one whose workgroup count is nearest four per CU (enough to
+  // even out chunks of unequal size, few partials to merge).
   if (dtype != SVG_BF16) return 1;
+  constexpr int64_t kCUs = 256;  // MI355X
   const int64_t chunks = (n_rows + kProfRows_bf16 - 1) / kProfRows_bf16;
   const int64_t wgs = chunks * g.B * g.H;
-  int64_t ks = (1024 + wgs - 1) / wgs;
   const int64_t nkt = (g.L + kBN_bf16 - 1) / kBN_bf16;
-  if (ks > 16) ks = 16;
-  if (ks > nkt) ks = nkt;
-  if (ks < 1) ks = 1;
-  return (int32_t)ks;
+  const int64_t kmax = nkt < 16 ? nkt : 16;
+  int64_t best = 1;
+  double best_t = 1e300;
+  for (int64_t ks = 1; ks <= kmax; ++ks) {
+    const double t = (double)((wgs * ks + kCUs - 1) / kCUs) / (double)ks;
+    const int64_t dist = wgs * ks > 4 * kCUs ? wgs * ks - 4 * kCUs : 4 * kCUs - wgs * ks;
+    const int64_t best_dist = wgs * best > 4 * kCUs ? wgs * best - 4 * kCUs : 4 * kCUs - wgs * best;
+    if (t < best_t - 1e-12 || (t < best_t + 1e-12 && dist < best_dist)) {
+      best_t = t;
+      best = ks;
+    }
+  }
+  return (int32_t)best;
 }
 
 // Layout: [profiling partials][labels][ranges][head order][permuted Q,K,V,O].
