@@ -64,22 +64,34 @@ __global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t k
                                                        const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        double* __restrict__ row_sums) {
+  constexpr int kMaxSplit = 16;
   const int r = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
   const int64_t row = (int64_t)bh * n_rows + r;
+  // the row's (m, l) pairs of every slice and state, staged once
+  __shared__ float ml[kMaxSplit * kMaxStates * 2];
+  const int nml = ksplit * nstates * 2;
+  for (int i = c; i < nml; i += D) ml[i] = part_ml[row * ksplit * nstates * 2 + i];
+  __syncthreads();
   float o[kMaxStates];
 #pragma unroll
   for (int st = 0; st < kMaxStates; ++st) {
     o[st] = 0.f;
     if (st >= nstates) continue;
     float m = -INFINITY;
-    for (int s = 0; s < ksplit; ++s) m = fmaxf(m, part_ml[((row * ksplit + s) * nstates + st) * 2]);
+    for (int s = 0; s < ksplit; ++s) m = fmaxf(m, ml[(s * nstates + st) * 2]);
+    if (m == -INFINITY) continue;
+    // all slices' accumulator loads first, then the sums in slice order
+    float acc[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s)
+      acc[s] = s < ksplit ? part_acc[((row * ksplit + s) * nstates + st) * D + c] : 0.f;
     float l = 0.f, a = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < ksplit; ++s) {
-        const int64_t slot = (row * ksplit + s) * nstates + st;
-        const float w = exp2f(part_ml[slot * 2] - m);
-        l += w * part_ml[slot * 2 + 1];
-        a += w * part_acc[slot * D + c];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      if (s < ksplit) {
+        const float w = exp2f(ml[(s * nstates + st) * 2] - m);
+        l += w * ml[(s * nstates + st) * 2 + 1];
+        a += w * acc[s];
       }
     }
     o[st] = l > 0.f ? a / l : 0.f;
