@@ -43,28 +43,27 @@ __global__ void k_build_ranges(KGeom g, const int32_t* __restrict__ modes, int32
 }
 
 // One workgroup: work of each head = listed tiles summed over its query
-// tiles; order = heads by descending work, ties by ascending index.
-__global__ void k_head_order(int32_t BH, int32_t nQT, const int32_t* __restrict__ ranges,
-                             int32_t* __restrict__ order) {
+// tiles (one wave per head, integer sums); order = heads by descending work,
+// ties by ascending index.
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void k_head_order(int32_t BH, int32_t nQT,
+                                                              const int32_t* __restrict__ ranges,
+                                                              int32_t* __restrict__ order) {
   extern __shared__ long long work[];  // BH entries
-  __shared__ long long part[256];
-  const int t = threadIdx.x;
-  for (int h = 0; h < BH; ++h) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int h = wave; h < BH; h += kOrderThreads / 64) {
     long long s = 0;
-    for (int qt = t; qt < nQT; qt += 256) {
+    for (int qt = lane; qt < nQT; qt += 64) {
       const int4 r = reinterpret_cast<const int4*>(ranges)[(int64_t)h * nQT + qt];
       s += (r.y - r.x) + (r.w - r.z);
     }
-    part[t] = s;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (t < w) part[t] += part[t + w];
-      __syncthreads();
-    }
-    if (t == 0) work[h] = part[0];
-    __syncthreads();
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) work[h] = s;
   }
-  for (int h = t; h < BH; h += 256) {
+  __syncthreads();
+  for (int h = t; h < BH; h += kOrderThreads) {
     int rank = 0;
     const long long wh = work[h];
     for (int o = 0; o < BH; ++o) rank += (work[o] > wh) || (work[o] == wh && o < h);
@@ -81,7 +80,7 @@ hipError_t launch_build_blocks(const KGeom& g, const int32_t* modes, int32_t BM,
   hipLaunchKernelGGL(k_build_ranges, dim3((unsigned)blocks), dim3(threads), 0, st, g, modes, BM, BN, nQT,
                      ranges);
   const int32_t BH = g.B * g.H;
-  hipLaunchKernelGGL(k_head_order, dim3(1), dim3(256), sizeof(long long) * BH, st, BH, nQT, ranges,
+  hipLaunchKernelGGL(k_head_order, dim3(1), dim3(kOrderThreads), sizeof(long long) * BH, st, BH, nQT, ranges,
                      head_order);
   return hipGetLastError();
 }

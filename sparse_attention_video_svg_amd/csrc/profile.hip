@@ -19,9 +19,15 @@
 
 namespace svg {
 
-// Position order of the sampled rows (ascending, distinct video rows):
-// rank = #rows with a smaller position j, plus #rows at the same position in
-// earlier frames.  Each count is a binary search per frame.
+// Position order of the sampled rows (ascending, distinct video rows): the
+// key of row x = T + i*F + j is its token-major index j*N + i, and its rank
+// is the number of rows with a smaller key (keys are distinct).
+// k_prof_rank_lds: all keys staged in LDS, each thread counts over them.
+// k_prof_rank (more rows than fit): per frame, a binary search for the
+// rows at smaller positions, plus the row at the same position if its
+// frame comes earlier.
+constexpr int kRankLdsRows = 8192;
+
 __device__ __forceinline__ int lower_bound_rows(const int32_t* rows, int n, int key) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -32,6 +38,32 @@ __device__ __forceinline__ int lower_bound_rows(const int32_t* rows, int n, int 
       hi = mid;
   }
   return lo;
+}
+
+__global__ __launch_bounds__(256) void k_prof_rank_lds(KGeom g, const int32_t* __restrict__ rows, int32_t n_rows,
+                                                        int32_t* __restrict__ ord_x, int32_t* __restrict__ ord_r) {
+  __shared__ __attribute__((aligned(16))) int32_t keys[kRankLdsRows];
+  const int n4 = (n_rows + 3) & ~3;
+  for (int r = threadIdx.x; r < n4; r += blockDim.x) {
+    int key = INT_MAX;
+    if (r < n_rows) {
+      const int u = rows[r] - g.T;
+      const int i = fastdiv(u, g.divF_mul, g.divF_shift);
+      key = (u - i * g.F) * g.N + i;
+    }
+    keys[r] = key;
+  }
+  __syncthreads();
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const int own = keys[r];
+  int rank = 0;
+  for (int o = 0; o < n4; o += 4) {
+    const int4 k4 = *reinterpret_cast<const int4*>(keys + o);
+    rank += (k4.x < own) + (k4.y < own) + (k4.z < own) + (k4.w < own);
+  }
+  ord_x[rank] = rows[r];
+  ord_r[rank] = r;
 }
 
 __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n_rows, int32_t* __restrict__ ord_x,
@@ -53,67 +85,78 @@ __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n
   ord_r[rank] = r;
 }
 
-// One workgroup (D threads, one per dim) per (sampled row, head): each of
-// the nstates states merged over the key slices and normalised, then the
-// row's sums over d: sum O_ref^2 at index ref, sum (O_s - O_ref)^2 at every
-// other index s.
+// One wave per (sampled row, head), D/64 dims per lane: each of the nstates
+// states merged over the key slices and normalised, then the row's sums
+// over d: sum O_ref^2 at index ref, sum (O_s - O_ref)^2 at every other index
+// s.  The (m, l) pairs are wave-uniform loads; each sum over d is the lane's
+// dims in order, then a fixed butterfly over the lanes.
 constexpr int kMaxStates = 4;
+constexpr int kMergeWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(D) void k_prof_merge_rows(int32_t n_rows, int32_t ksplit, int32_t nstates, int32_t ref,
-                                                       const float* __restrict__ part_acc,
-                                                       const float* __restrict__ part_ml,
-                                                       double* __restrict__ row_sums) {
+__global__ __launch_bounds__(64 * kMergeWaves) void k_prof_merge_rows(int64_t total_rows, int32_t ksplit,
+                                                                      int32_t nstates, int32_t ref,
+                                                                      const float* __restrict__ part_acc,
+                                                                      const float* __restrict__ part_ml,
+                                                                      double* __restrict__ row_sums) {
   constexpr int kMaxSplit = 16;
-  const int r = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
-  const int64_t row = (int64_t)bh * n_rows + r;
-  // the row's (m, l) pairs of every slice and state, staged once
-  __shared__ float ml[kMaxSplit * kMaxStates * 2];
-  const int nml = ksplit * nstates * 2;
-  for (int i = c; i < nml; i += D) ml[i] = part_ml[row * ksplit * nstates * 2 + i];
-  __syncthreads();
-  float o[kMaxStates];
+  constexpr int PL = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + wave;  // bh * n_rows + r
+  if (row >= total_rows) return;
+  const float* ml = part_ml + row * ksplit * nstates * 2;
+  float o[kMaxStates][PL];
 #pragma unroll
   for (int st = 0; st < kMaxStates; ++st) {
-    o[st] = 0.f;
+#pragma unroll
+    for (int p = 0; p < PL; ++p) o[st][p] = 0.f;
     if (st >= nstates) continue;
     float m = -INFINITY;
     for (int s = 0; s < ksplit; ++s) m = fmaxf(m, ml[(s * nstates + st) * 2]);
     if (m == -INFINITY) continue;
     // all slices' accumulator loads first, then the sums in slice order
-    float acc[kMaxSplit];
+    float acc[kMaxSplit][PL];
 #pragma unroll
     for (int s = 0; s < kMaxSplit; ++s)
-      acc[s] = s < ksplit ? part_acc[((row * ksplit + s) * nstates + st) * D + c] : 0.f;
-    float l = 0.f, a = 0.f;
+#pragma unroll
+      for (int p = 0; p < PL; ++p)
+        acc[s][p] = s < ksplit ? part_acc[((row * ksplit + s) * nstates + st) * D + PL * lane + p] : 0.f;
+    float l = 0.f, a[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) a[p] = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxSplit; ++s) {
       if (s < ksplit) {
         const float w = exp2f(ml[(s * nstates + st) * 2] - m);
         l += w * ml[(s * nstates + st) * 2 + 1];
-        a += w * acc[s];
+#pragma unroll
+        for (int p = 0; p < PL; ++p) a[p] += w * acc[s][p];
       }
     }
-    o[st] = l > 0.f ? a / l : 0.f;
-  }
-  float o_ref = o[0];
 #pragma unroll
-  for (int st = 1; st < kMaxStates; ++st) o_ref = st == ref ? o[st] : o_ref;
-  __shared__ double red[kMaxStates][D];
+    for (int p = 0; p < PL; ++p) o[st][p] = l > 0.f ? a[p] / l : 0.f;
+  }
+  float o_ref[PL];
+#pragma unroll
+  for (int p = 0; p < PL; ++p) {
+    o_ref[p] = o[0][p];
+#pragma unroll
+    for (int st = 1; st < kMaxStates; ++st) o_ref[p] = st == ref ? o[st][p] : o_ref[p];
+  }
 #pragma unroll
   for (int st = 0; st < kMaxStates; ++st) {
-    const double dd = st == ref ? (double)o_ref : (double)o[st] - (double)o_ref;
-    red[st][c] = dd * dd;
-  }
-  __syncthreads();
-  for (int w = D / 2; w > 0; w >>= 1) {
-    if (c < w) {
+    if (st >= nstates) break;
+    double sum = 0.0;
 #pragma unroll
-      for (int k = 0; k < kMaxStates; ++k) red[k][c] += red[k][c + w];
+    for (int p = 0; p < PL; ++p) {
+      const double dd = st == ref ? (double)o_ref[p] : (double)o[st][p] - (double)o_ref[p];
+      sum += dd * dd;
     }
-    __syncthreads();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) row_sums[row * nstates + st] = sum;
   }
-  if (c < nstates) row_sums[row * nstates + c] = red[c][0];
 }
 
 // Per-head fixed-order sums of the row sums (one workgroup per head).
@@ -192,21 +235,28 @@ __global__ __launch_bounds__(256) void k_search_finalize(int32_t d, int32_t n_ro
 
 hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_prof_rank, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, st, g, rows, n_rows, ord_x,
-                     ord_r);
+  const dim3 grid((unsigned)((n_rows + 255) / 256));
+  if (n_rows <= kRankLdsRows)
+    hipLaunchKernelGGL(k_prof_rank_lds, grid, dim3(256), 0, st, g, rows, n_rows, ord_x, ord_r);
+  else
+    hipLaunchKernelGGL(k_prof_rank, grid, dim3(256), 0, st, g, rows, n_rows, ord_x, ord_r);
   return hipGetLastError();
 }
 
 hipError_t launch_prof_merge(const KGeom& g, int32_t n_rows, int32_t ksplit, int32_t nstates, int32_t ref,
                              const float* part_acc, const float* part_ml, double* row_sums, hipStream_t st) {
   if (nstates < 1 || nstates > kMaxStates) return hipErrorInvalidValue;
-  dim3 grid((unsigned)n_rows, (unsigned)(g.B * g.H));
+  if (ksplit < 1 || ksplit > 16) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)g.B * g.H * n_rows;
+  const int64_t blocks = (total + kMergeWaves - 1) / kMergeWaves;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(64 * kMergeWaves);
   if (g.d == 64)
-    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, dim3(64), 0, st, n_rows, ksplit, nstates, ref, part_acc, part_ml,
+    hipLaunchKernelGGL(k_prof_merge_rows<64>, grid, block, 0, st, total, ksplit, nstates, ref, part_acc, part_ml,
                        row_sums);
   else
-    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, dim3(128), 0, st, n_rows, ksplit, nstates, ref, part_acc,
-                       part_ml, row_sums);
+    hipLaunchKernelGGL(k_prof_merge_rows<128>, grid, block, 0, st, total, ksplit, nstates, ref, part_acc, part_ml,
+                       row_sums);
   return hipGetLastError();
 }
 
