@@ -31,6 +31,12 @@ FP8_SCORES = 4   # svg_layer_forward: scores on FP8 E4M3 Q and K
 FP8_PV = 8       # with FP8_SCORES: P.V on FP8 E4M3 weights and V as well
 SEARCH_CANDIDATES = (SKIP, WINDOW, TEMPORAL, STRIPE)  # order of svg_search_modes' stats
 
+# The library trusts device-side contents (sampled rows, modes, tile ranges,
+# head order).  With DEBUG true (or SVG_DEBUG=1 in the environment) the
+# binding copies them to the host and validates them before each call; this
+# synchronises the device.
+DEBUG = os.environ.get("SVG_DEBUG", "") not in ("", "0")
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # SVG_LIBRARY may point at another build of the same library (A/B timing).
 _LIB_PATH = os.environ.get("SVG_LIBRARY") or os.path.join(_HERE, "libsvg.so")
@@ -208,6 +214,79 @@ def _check_shape(geom, t, name):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _check_vec(t, name, dtype, n, optional=False):
+    """Metadata of a small device vector: dtype, contiguity, length >= n."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {n}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _t_i32():
+    import torch
+    return torch.int32
+
+
+def _t_f32():
+    import torch
+    return torch.float32
+
+
+def _check_tile_args(geom, BM, BN, modes, ranges, head_order):
+    BH = geom.B * geom.H
+    _check_vec(modes, "modes", _t_i32(), BH)
+    _check_vec(ranges, "ranges", _t_i32(), BH * -(-geom.L // BM) * 4)
+    _check_vec(head_order, "head_order", _t_i32(), BH)
+    if DEBUG:
+        _debug_modes(geom, modes)
+        _debug_tiles(geom, BM, BN, ranges, head_order)
+
+
+def _debug_rows(geom, rows):
+    """Sampled rows: strictly ascending video rows in [T, L)."""
+    r = rows.detach().to("cpu").long()
+    if r.numel() == 0:
+        raise ValueError("rows is empty")
+    if int(r[0]) < geom.T or int(r[-1]) >= geom.L:
+        raise ValueError(f"rows must lie in [T, L) = [{geom.T}, {geom.L}), got [{int(r[0])}, {int(r[-1])}]")
+    if r.numel() > 1 and not bool((r[1:] > r[:-1]).all()):
+        raise ValueError("rows must be strictly ascending (distinct, sorted)")
+
+
+def _debug_modes(geom, modes):
+    m = modes.detach().to("cpu")[: geom.B * geom.H]
+    bad = (m < SPATIAL) | (m > STRIPE)
+    if bool(bad.any()):
+        i = int(bad.nonzero()[0])
+        raise ValueError(f"modes[{i}] = {int(m[i])} is not a mode (0..5)")
+
+
+def _debug_tiles(geom, BM, BN, ranges, head_order):
+    """Tile ranges: per (head, query tile) [x, y) U [z, w) within the key
+    tiles, the second empty (z = w) or after the first (y <= z); head order:
+    a permutation of the heads."""
+    import torch
+    BH = geom.B * geom.H
+    nq, nk = -(-geom.L // BM), -(-geom.L // BN)
+    r = ranges.detach().to("cpu")[: BH * nq * 4].view(-1, 4).long()
+    x, y, z, w = r.unbind(1)
+    ok = (0 <= x) & (x <= y) & (y <= nk) & (0 <= z) & (z <= w) & (w <= nk) & ((z == w) | (y <= z))
+    if not bool(ok.all()):
+        i = int((~ok).nonzero()[0])
+        raise ValueError(f"ranges entry {i} = {r[i].tolist()} is not two ordered ranges within {nk} key tiles")
+    o = head_order.detach().to("cpu")[:BH].long()
+    if not bool((o.sort().values == torch.arange(BH)).all()):
+        raise ValueError("head_order is not a permutation of the heads")
+
+
 def svg_abi_version():
     return _lib().svg_abi_version()
 
@@ -235,6 +314,12 @@ def svg_profile_heads(geom, q, k, v, rows, labels, stats, ws, fallback_rel_mse=0
         _check_shape(geom, t, name)
     if k.stride() != q.stride() or v.stride() != q.stride():
         raise ValueError("q, k and v must share strides")
+    BH = geom.B * geom.H
+    _check_vec(rows, "rows", _t_i32(), 1)
+    _check_vec(labels, "labels", _t_i32(), BH)
+    _check_vec(stats, "stats", _t_f32(), BH * 3)
+    if DEBUG:
+        _debug_rows(geom, rows)
     g = geom.c()
     _check(_lib().svg_profile_heads(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _strides(q),
                                     _ptr(rows), rows.numel(), float(fallback_rel_mse), _ptr(labels), _ptr(stats),
@@ -248,6 +333,12 @@ def svg_search_modes(geom, q, k, v, rows, modes_out, stats_out, ws, lam=0.5, eps
         _check_shape(geom, t, name)
     if k.stride() != q.stride() or v.stride() != q.stride():
         raise ValueError("q, k and v must share strides")
+    BH = geom.B * geom.H
+    _check_vec(rows, "rows", _t_i32(), 1)
+    _check_vec(modes_out, "modes_out", _t_i32(), BH)
+    _check_vec(stats_out, "stats_out", _t_f32(), BH * 8)
+    if DEBUG:
+        _debug_rows(geom, rows)
     g = geom.c()
     _check(_lib().svg_search_modes(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _strides(q),
                                    _ptr(rows), rows.numel(), float(lam), float(eps), int(penalty), _ptr(modes_out),
@@ -255,6 +346,13 @@ def svg_search_modes(geom, q, k, v, rows, modes_out, stats_out, ws, lam=0.5, eps
 
 
 def svg_build_blocks(geom, modes, BM, BN, ranges, head_order, stream=None):
+    BH = geom.B * geom.H
+    _check_vec(modes, "modes", _t_i32(), BH)
+    if BM > 0 and BN > 0:
+        _check_vec(ranges, "ranges", _t_i32(), BH * -(-geom.L // BM) * 4)
+    _check_vec(head_order, "head_order", _t_i32(), BH)
+    if DEBUG:
+        _debug_modes(geom, modes)
     g = geom.c()
     _check(_lib().svg_build_blocks(ctypes.byref(g), _ptr(modes), BM, BN, _ptr(ranges), _ptr(head_order),
                                    _stream(stream)))
@@ -265,6 +363,9 @@ def svg_layout_permute(geom, src, dst, modes=None, inverse=False, stream=None):
     _check_shape(geom, dst, "dst")
     if src.dtype != dst.dtype:
         raise TypeError("src and dst dtypes differ")
+    _check_vec(modes, "modes", _t_i32(), geom.B * geom.H, optional=True)
+    if DEBUG and modes is not None:
+        _debug_modes(geom, modes)
     g = geom.c()
     _check(_lib().svg_layout_permute(ctypes.byref(g), _dtype_code(src), _ptr(src), _strides(src), _ptr(dst),
                                      _strides(dst), _ptr(modes), 1 if inverse else 0, _stream(stream)))
@@ -280,6 +381,7 @@ def svg_sparse_attention(geom, q, k, v, o, modes, ranges, head_order, qp=None, k
         raise ValueError("qp, kp and vp must share strides")
     din = _dtype_code(q)
     BM, BN = svg_tile_config(din, geom.d)
+    _check_tile_args(geom, BM, BN, modes, ranges, head_order)
     g = geom.c()
     _check(_lib().svg_sparse_attention(
         ctypes.byref(g), din, _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(qp), _ptr(kp), _ptr(vp),
@@ -295,6 +397,9 @@ def svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk, stream=None):
     _check_shape(geom, k, "k")
     if k.stride() != q.stride():
         raise ValueError("q and k must share strides")
+    _check_vec(modes, "modes", _t_i32(), geom.B * geom.H)
+    if DEBUG:
+        _debug_modes(geom, modes)
     g = geom.c()
     _check(_lib().svg_quantize_qk(ctypes.byref(g), _dtype_code(q), _ptr(q), _ptr(k), _strides(q), _ptr(modes),
                                   _ptr(q8), _ptr(sq), _ptr(k8), _ptr(sk), _stream(stream)))
@@ -304,6 +409,7 @@ def svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, head_ord
     _check_shape(geom, v, "v")
     _check_shape(geom, o, "o")
     BM, BN = svg_tile_config(BF16, geom.d)
+    _check_tile_args(geom, BM, BN, modes, ranges, head_order)
     g = geom.c()
     _check(_lib().svg_sparse_attention_fp8(ctypes.byref(g), _dtype_code(o), _ptr(q8), _ptr(sq), _ptr(k8), _ptr(sk),
                                            _ptr(v), _strides(v), _ptr(o), _strides(o), _ptr(modes), _ptr(ranges),
@@ -315,6 +421,9 @@ def svg_quantize_v(geom, v, modes, v8, sv, stream=None):
     tile of the working layout, transposed: v8 uint8 [B*H*ceil(L/64)*d*64];
     sv float32 [B*H]."""
     _check_shape(geom, v, "v")
+    _check_vec(modes, "modes", _t_i32(), geom.B * geom.H)
+    if DEBUG:
+        _debug_modes(geom, modes)
     g = geom.c()
     _check(_lib().svg_quantize_v(ctypes.byref(g), _dtype_code(v), _ptr(v), _strides(v), _ptr(modes), _ptr(v8),
                                  _ptr(sv), _stream(stream)))
@@ -323,6 +432,7 @@ def svg_quantize_v(geom, v, modes, v8, sv, stream=None):
 def svg_sparse_attention_fp8_pv(geom, q8, sq, k8, sk, v8, sv, o, modes, ranges, head_order, stream=None):
     _check_shape(geom, o, "o")
     BM, BN = svg_tile_config(BF16, geom.d)
+    _check_tile_args(geom, BM, BN, modes, ranges, head_order)
     g = geom.c()
     _check(_lib().svg_sparse_attention_fp8_pv(ctypes.byref(g), _dtype_code(o), _ptr(q8), _ptr(sq), _ptr(k8),
                                               _ptr(sk), _ptr(v8), _ptr(sv), _ptr(o), _strides(o), _ptr(modes),
@@ -335,6 +445,16 @@ def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_ou
         _check_shape(geom, t, name)
     if k.stride() != q.stride() or v.stride() != q.stride():
         raise ValueError("q, k and v must share strides")
+    BH = geom.B * geom.H
+    _check_vec(rows, "rows", _t_i32(), 1, optional=True)
+    _check_vec(modes_in, "modes_in", _t_i32(), BH, optional=True)
+    _check_vec(labels_out, "labels_out", _t_i32(), BH, optional=True)
+    _check_vec(stats_out, "stats_out", _t_f32(), BH * 3, optional=True)
+    if DEBUG:
+        if rows is not None:
+            _debug_rows(geom, rows)
+        if modes_in is not None:
+            _debug_modes(geom, modes_in)
     g = geom.c()
     n_rows = 0 if rows is None else rows.numel()
     _check(_lib().svg_layer_forward(

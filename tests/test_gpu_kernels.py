@@ -262,3 +262,31 @@ def test_profile_strided_batched(n_rows_frac, seed):
         want, ref = oracle.profile_head(og, inp["q"][bh], inp["k"][bh], inp["v"][bh], scale_of(g), rows_np)
         assert lab[bh] == want, (bh, lab[bh], want, st[bh], ref)
         np.testing.assert_allclose(st[bh], ref, rtol=2e-2, atol=1e-4)
+
+
+def test_profile_more_rows_than_lds_order():
+    """More sampled rows (about 8900) than the position-order kernel stages in
+    LDS (8192): the temporal sweep then takes its row order from per-frame
+    binary searches in global memory.  Labels bit-exact, statistics as above."""
+    N, F, T, d, a1, a2 = 3, 3500, 0, 64, 1, 40
+    kinds = [S.TEMPORAL, S.SPATIAL, S.UNSTRUCTURED]
+    H = len(kinds)
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2)
+    inp = S.small_config(N, F, T, H, d, a1, a2, kinds, seed=61)
+    q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
+    rows_np = S.sample_rows(N, F, T, 0.85, 9)
+    assert rows_np.size > 8192
+    rows = torch.from_numpy(rows_np).cuda()
+    labels = torch.empty(H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(H * 3, dtype=torch.float32, device="cuda")
+    ws = svg.alloc_workspace(g, svg.BF16, rows.numel(), svg.VIRTUAL_PERMUTE)
+    print(f"\n[profile rows={rows_np.size}]", flush=True)
+    svg.svg_profile_heads(g, q, k, v, rows, labels, stats, ws)
+    torch.cuda.synchronize()
+    lab = labels.cpu().numpy()
+    st = stats.cpu().numpy().reshape(H, 3)
+    og = ogeom(g)
+    for h in range(H):
+        want, ref = oracle.profile_head(og, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows_np)
+        assert lab[h] == want, (h, lab[h], want, st[h], ref)
+        np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
