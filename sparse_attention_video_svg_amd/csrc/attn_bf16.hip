@@ -132,10 +132,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_attn_bf16(
 }
 
 // Partial (m, l, acc) of one output of one sampled row: acc in the
-// accumulator layout order is written back to dims order.
+// accumulator layout order is written back to dims order.  A row with no key
+// in the slice (m = -inf) writes only (m, l); the merge skips its acc.
 template <int D>
 __device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, float* ml, int hh) {
   const float l_tot = half_sum(st.l_part);
+  if (hh == 0) {
+    ml[0] = st.m_ref;
+    ml[1] = l_tot;
+  }
+  if (st.m_ref == -INFINITY) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -144,10 +150,6 @@ __device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, fl
       *reinterpret_cast<f32x4*>(acc + d0) =
           f32x4{st.o[db][4 * g4], st.o[db][4 * g4 + 1], st.o[db][4 * g4 + 2], st.o[db][4 * g4 + 3]};
     }
-  if (hh == 0) {
-    ml[0] = st.m_ref;
-    ml[1] = l_tot;
-  }
 }
 
 // ---------------------------------------------------------------------------

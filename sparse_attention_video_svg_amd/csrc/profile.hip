@@ -115,13 +115,16 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_prof_merge_rows(int64_t to
     float m = -INFINITY;
     for (int s = 0; s < ksplit; ++s) m = fmaxf(m, ml[(s * nstates + st) * 2]);
     if (m == -INFINITY) continue;
-    // all slices' accumulator loads first, then the sums in slice order
+    // all slices' accumulator loads first (none for slices the row has no
+    // key in: their acc is not written), then the sums in slice order
     float acc[kMaxSplit][PL];
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s)
+    for (int s = 0; s < kMaxSplit; ++s) {
+      const bool has = s < ksplit && ml[(s * nstates + st) * 2] != -INFINITY;
 #pragma unroll
       for (int p = 0; p < PL; ++p)
-        acc[s][p] = s < ksplit ? part_acc[((row * ksplit + s) * nstates + st) * D + PL * lane + p] : 0.f;
+        acc[s][p] = has ? part_acc[((row * ksplit + s) * nstates + st) * D + PL * lane + p] : 0.f;
+    }
     float l = 0.f, a[PL];
 #pragma unroll
     for (int p = 0; p < PL; ++p) a[p] = 0.f;
