@@ -22,9 +22,14 @@ KINDS5 = [S.FULL, S.SKIP, S.WINDOW, S.TEMPORAL, S.STRIPE]
 RTOL, ATOL = 2e-2, 1e-5
 
 
-def run_search(g, inp, rows_np, lam, eps, penalty):
+def run_search(g, inp, rows_np, lam, eps, penalty, interleaved=False):
     BH = g.B * g.H
-    q, k, v = (to_device(inp[n].reshape(g.B, g.H, g.L, g.d), torch.bfloat16) for n in "qkv")
+    if interleaved:  # [B, L, H, d] memory viewed as [B, H, L, d]
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[n].reshape(g.B, g.H, g.L, g.d).transpose(0, 2, 1, 3)))
+                   .to(torch.bfloat16).cuda().permute(0, 2, 1, 3) for n in "qkv")
+        assert q.stride() == (g.L * g.H * g.d, g.d, g.H * g.d, 1)
+    else:
+        q, k, v = (to_device(inp[n].reshape(g.B, g.H, g.L, g.d), torch.bfloat16) for n in "qkv")
     rows = torch.from_numpy(rows_np.astype(np.int32)).cuda()
     ws = svg.alloc_workspace(g, svg.BF16, rows.numel(), svg.MODE_SEARCH)
     modes = torch.full((BH,), -1, dtype=torch.int32, device="cuda")
@@ -97,3 +102,19 @@ def test_search_sparse_vdit_shape(lam):
         for h, kd in enumerate(kinds):
             if kd in want:
                 assert modes[h] == want[kd], (h, kd, modes[h], stats[h])
+
+
+def test_search_strided_equals_contiguous():
+    """Token-interleaved [B, L, H, d] inputs (B = 2, text prefix): modes and
+    statistics bit-identical to the contiguous run, which the tests above
+    hold to the oracle."""
+    B, N, F, T, d = 2, 6, 50, 5, 128
+    H = len(KINDS5)
+    g = svg.Geom(B=B, H=H, d=d, N=N, F=F, T=T, a1=2, a2=8, window=F, stripe=40)
+    inp = S.small_config(N, F, T, B * H, d, 2, 8, KINDS5 * B, seed=77, window=F, stripe=40)
+    rows_np = S.sample_rows(N, F, T, 0.3, 5)
+    print(f"\n[search strided B={B} N={N} F={F} T={T}]", flush=True)
+    m0, s0 = run_search(g, inp, rows_np, 0.5, 1.0, 0)
+    m1, s1 = run_search(g, inp, rows_np, 0.5, 1.0, 0, interleaved=True)
+    assert np.array_equal(m0, m1)
+    assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
