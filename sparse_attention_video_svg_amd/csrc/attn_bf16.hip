@@ -93,8 +93,11 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   }
 }
 
+// d 64: registers capped at 128 (four waves per SIMD), so that two
+// workgroups share a CU and, not being in lock step, overlap one's softmax
+// with the other's MFMAs (the softmax outweighs the MFMAs at d 64)
 template <int D, bool OUT_BF16, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT,
+__global__ __launch_bounds__(64 * WAVES, (D == 64 ? 4 : WAVES <= 6 ? 2 : 1)) void k_attn_bf16(KGeom g, AttnPtrs a, int32_t nQT,
                                                                                 int32_t total) {
   using C = TileCfg<D, WAVES>;
   constexpr int BMW = 32 * WAVES;
