@@ -540,7 +540,7 @@ struct Fp8Ptrs {
 };
 
 template <int D, bool OUT_BF16, bool VIRT, int WAVES>
-__device__ __forceinline__ void attn_tile_fp8(const KGeom& g, const Fp8Ptrs& a, int bh, int qt, int mode, int nQT,
+__device__ __forceinline__ void attn_tile_fp8(const KGeom& g, const Fp8Ptrs& a, int bh, int qt, int rq, int mode, int nQT,
                                               uint8_t* lds_k, __bf16* lds_v, int wave, int lane) {
   constexpr int BMW = 32 * WAVES;
   const int hh = lane >> 5;
@@ -550,7 +550,7 @@ __device__ __forceinline__ void attn_tile_fp8(const KGeom& g, const Fp8Ptrs& a, 
   constexpr int OE = OUT_BF16 ? 2 : 4;
   auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
 
-  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
+  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + rq];
   Fp8Loader<D, VIRT, WAVES> ld;
   ld.init(a.k8 + (int64_t)bh * g.L * D, static_cast<const __bf16*>(a.v) + vbase, a.sv.x, g.L);
 
@@ -594,7 +594,7 @@ __device__ __forceinline__ void attn_tile_fp8(const KGeom& g, const Fp8Ptrs& a, 
 
 // One query tile with FP8 P.V (Q8, O through the index map for TEMPORAL heads).
 template <int D, bool OUT_BF16, bool VIRT, int WAVES>
-__device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a, int bh, int qt, int mode, int nQT,
+__device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a, int bh, int qt, int rq, int mode, int nQT,
                                                 uint8_t* lds_k, uint8_t* lds_v, int wave, int lane) {
   constexpr int BMW = 32 * WAVES;
   const int hh = lane >> 5;
@@ -603,7 +603,7 @@ __device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a
   constexpr int OE = OUT_BF16 ? 2 : 4;
   auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
 
-  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
+  const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + rq];
   Fp8PvLoader<D, WAVES> ld;
   ld.kb = a.k8 + (int64_t)bh * g.L * D;
   ld.vb = a.v8 + (int64_t)bh * a.nKT * V8Cfg<D>::TILE_BYTES;
@@ -647,9 +647,16 @@ __device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a
   }
 }
 
+// WAVES = 4 (FP8 P.V): a workgroup takes half of a 256-row query tile (with
+// that tile's key-tile ranges); three workgroups share a CU and, not being in
+// lock step, one's softmax runs under another's MFMAs (all products are FP8
+// there, so the softmax outweighs them).  FP8 scores with bf16 P.V keep 8
+// waves (measured faster).
 template <int D, bool OUT_BF16, int WAVES, bool PV8>
-__global__ __launch_bounds__(64 * WAVES, 1) void k_attn_fp8(KGeom g, Fp8Ptrs a, int32_t nQT, int32_t total) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 3 : 1) void k_attn_fp8(KGeom g, Fp8Ptrs a, int32_t nQT,
+                                                                           int32_t total) {
   constexpr int BMW = 32 * WAVES;
+  constexpr int SPLIT = kBM_bf16 / BMW;  // workgroups per ranges tile
   extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
   uint8_t* lds_k = lds8;  // [2][TILE_BYTES], then two V tiles (bf16 or V8)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -658,8 +665,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_attn_fp8(KGeom g, Fp8Ptrs a, 
   const int xcd = w & 7, slot = w >> 3;
   const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
   if (logical >= total) return;
-  const int bh = a.order[logical / nQT];
-  const int qt = logical % nQT;
+  const int bh = a.order[logical / (nQT * SPLIT)];
+  const int qt = logical % (nQT * SPLIT), rq = qt / SPLIT;
   const int mode = a.modes[bh];
   if (mode == SVG_SKIP) {
     constexpr int OE = OUT_BF16 ? 2 : 4;
@@ -677,15 +684,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_attn_fp8(KGeom g, Fp8Ptrs a, 
   if constexpr (PV8) {
     uint8_t* lds_v = lds8 + 2 * Fp8Cfg<D>::TILE_BYTES;
     if (mode == SVG_TEMPORAL)
-      attn_tile_fp8pv<D, OUT_BF16, true, WAVES>(g, a, bh, qt, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8pv<D, OUT_BF16, true, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
     else
-      attn_tile_fp8pv<D, OUT_BF16, false, WAVES>(g, a, bh, qt, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8pv<D, OUT_BF16, false, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
   } else {
     __bf16* lds_v = reinterpret_cast<__bf16*>(lds8 + 2 * Fp8Cfg<D>::TILE_BYTES);
     if (mode == SVG_TEMPORAL)
-      attn_tile_fp8<D, OUT_BF16, true, WAVES>(g, a, bh, qt, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8<D, OUT_BF16, true, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
     else
-      attn_tile_fp8<D, OUT_BF16, false, WAVES>(g, a, bh, qt, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8<D, OUT_BF16, false, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
   }
 }
 
@@ -723,7 +730,7 @@ hipError_t launch_quant_v(const KGeom& g, const void* v, svg_strides s, const in
 template <int D, bool OUT_BF16, bool PV8>
 static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int64_t grid, int64_t total,
                              hipStream_t st) {
-  constexpr int W = kAttnWaves;
+  constexpr int W = PV8 ? 4 : kAttnWaves;
   const size_t vtile = PV8 ? (size_t)V8Cfg<D>::TILE_BYTES : (size_t)TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   const size_t lds = 2 * (size_t)Fp8Cfg<D>::TILE_BYTES + 2 * vtile;
   auto kern = k_attn_fp8<D, OUT_BF16, W, PV8>;
@@ -736,7 +743,8 @@ static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int6
 template <bool PV8>
 static hipError_t launch_fp8_d(const KGeom& g, const Fp8Ptrs& a, bool out_bf16, hipStream_t st) {
   const int32_t nQT = (g.L + kBM_bf16 - 1) / kBM_bf16;
-  const int64_t total = (int64_t)g.B * g.H * nQT;
+  // FP8 P.V: two 128-row workgroups per ranges tile
+  const int64_t total = (int64_t)g.B * g.H * nQT * (PV8 ? 2 : 1);
   const int64_t per_round = 8 * kXcdRun;
   const int64_t grid = (total + per_round - 1) / per_round * per_round;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
