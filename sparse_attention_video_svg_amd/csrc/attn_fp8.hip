@@ -19,6 +19,10 @@
 //  * TEMPORAL heads read Q8 and V in natural order through the token-major
 //    index map (no permuted copies); K8 is written in token-major order by
 //    the quantisation kernel, so its tiles are contiguous.
+//  * Workgroups: 8 waves x 32 rows, one per CU, as in the bf16 kernel; with
+//    FP8 P.V (every product on the FP8 matrix cores, so the softmax
+//    outweighs them) 4 waves taking half of a 256-row query tile, three per
+//    CU, out of lock step.
 #include "attn_common.h"
 
 namespace svg {
