@@ -77,6 +77,43 @@ def test_profile_matches_numpy(oracle_lib, T):
         np.testing.assert_allclose(st, st_np, rtol=1e-10, atol=1e-300)
 
 
+@pytest.mark.parametrize("N,F,T,a1,a2", [(4, 12, 0, 1, 2), (5, 9, 3, 2, 3), (3, 16, 2, 1, 16)])
+def test_profile_uniform_weights_closed_form(oracle_lib, N, F, T, a1, a2):
+    """Q = 0 makes every score equal, so each masked attention output is the
+    plain mean of V over the row's active keys (text keys plus the frames
+    within a1, or the positions within a2 in every frame).  The statistics
+    then follow from means alone: rel_m = sum (mean_m - mean_all)^2 /
+    sum mean_all^2 over rows x d, and the third entry mean(mean_all^2)."""
+    d = 8
+    L = T + N * F
+    rng = np.random.default_rng(N * F + T)
+    q = np.zeros((L, d), np.float32)
+    k = rng.standard_normal((L, d)).astype(np.float32)
+    v = (rng.standard_normal((L, d)) + 0.5).astype(np.float32)
+    rows = np.arange(T, L, 2)
+    g = oracle.geom(N, F, T, a1, a2)
+    label, st = oracle.profile_head(g, q, k, v, 0.7, rows)
+
+    def keys(x, mode):
+        i, j = divmod(x - T, F)
+        ks = list(range(T))
+        for x2 in range(T, L):
+            i2, j2 = divmod(x2 - T, F)
+            if (mode == "s" and abs(i2 - i) < a1) or (mode == "t" and abs(j2 - j) < a2):
+                ks.append(x2)
+        return ks
+
+    vd = v.astype(np.float64)
+    full = np.repeat(vd.mean(axis=0)[None], rows.size, axis=0)
+    spat = np.stack([vd[keys(x, "s")].mean(axis=0) for x in rows])
+    temp = np.stack([vd[keys(x, "t")].mean(axis=0) for x in rows])
+    den = (full ** 2).sum()
+    want = [((spat - full) ** 2).sum() / den, ((temp - full) ** 2).sum() / den, (full ** 2).mean()]
+    np.testing.assert_allclose(st, want, rtol=1e-12, atol=1e-15)
+    rs, rt = want[0], want[1]
+    assert label == (oracle.FULL if min(rs, rt) >= 0.05 else oracle.SPATIAL if rs <= rt else oracle.TEMPORAL)
+
+
 MODES = [oracle.SPATIAL, oracle.TEMPORAL, oracle.FULL, oracle.SKIP, oracle.WINDOW, oracle.STRIPE]
 
 

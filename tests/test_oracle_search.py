@@ -141,3 +141,45 @@ def test_skip_error_is_the_mean_square_of_full_attention():
     _, mse, _, _ = oracle.search_head(g, inp["q"][0], inp["k"][0], inp["v"][0], 1 / 8, rows)
     _, stats = oracle.profile_head(g, inp["q"][0], inp["k"][0], inp["v"][0], 1 / 8, rows)
     assert math.isclose(mse[0], stats[2], rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("N,F,T,W,St,a2", [(4, 12, 0, 5, 7, 2), (3, 10, 3, 11, 4, 3), (5, 6, 2, 40, 100, 6)])
+def test_uniform_weights_closed_form(N, F, T, W, St, a2):
+    """Q = 0 makes every score equal, so each candidate's output is the plain
+    mean of V over the row's active keys (text keys plus |u1 - u2| < W for
+    the diagonal, |j1 - j2| < a2 for the multi-diagonal, u2 < stripe for the
+    stripe) and skip's output is 0.  The MSEs against full attention, the
+    sparsities (from the masks' pair counts) and the losses follow."""
+    d = 8
+    L = T + N * F
+    rng = np.random.default_rng(N * F + T + W)
+    q = np.zeros((L, d), np.float32)
+    k = rng.standard_normal((L, d)).astype(np.float32)
+    v = (rng.standard_normal((L, d)) - 0.25).astype(np.float32)
+    rows = np.arange(0, L, 2)
+    g = oracle.geom(N, F, T, a1=1, a2=a2, window=W, stripe=St)
+    lam = 0.3
+    mode, mse, loss, sp = oracle.search_head(g, q, k, v, 0.5, rows, lam=lam, eps=10.0)
+
+    def active(x1, x2, c):
+        if x1 < T or x2 < T:
+            return True
+        u1, u2 = x1 - T, x2 - T
+        if c == "w":
+            return abs(u1 - u2) < W
+        if c == "t":
+            return abs(u1 % F - u2 % F) < a2
+        return u2 < St
+
+    vd = v.astype(np.float64)
+    full = np.repeat(vd.mean(axis=0)[None], rows.size, axis=0)
+    want_mse, want_sp = [float((full ** 2).mean())], [1.0]
+    for c in "wts":
+        out = np.stack([vd[[x2 for x2 in range(L) if active(x, x2, c)]].mean(axis=0) for x in rows])
+        want_mse.append(float(((out - full) ** 2).mean()))
+        nnz = sum(active(x1, x2, c) for x1 in range(L) for x2 in range(L))
+        want_sp.append(1.0 - nnz / L ** 2)
+    np.testing.assert_allclose(mse, want_mse, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(sp, want_sp, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(loss, np.array(want_mse) + lam * (1.0 - np.array(want_sp)), rtol=1e-12, atol=1e-16)
+    assert mode == oracle.SEARCH_CANDIDATES[int(np.argmin(loss))]
