@@ -94,3 +94,40 @@ def test_profile_statistics_from_means(N, F, T, d, a1, a2):
         rs, rt = want[0], want[1]
         if abs(rs - rt) > 0.01 * max(rs, rt) and abs(min(rs, rt) - 0.05) > 1e-3:
             assert lab[h] == (svg.FULL if min(rs, rt) >= 0.05 else svg.SPATIAL if rs <= rt else svg.TEMPORAL)
+
+
+@pytest.mark.parametrize("N,F,T,d,W,St,a2", [(5, 40, 0, 128, 40, 64, 6), (4, 48, 5, 64, 20, 30, 48)])
+def test_search_mse_from_means(N, F, T, d, W, St, a2):
+    """svg_search_modes with Q = 0: each candidate's MSE against full
+    attention over the sampled rows follows from means of V (skip: mean of
+    O_full^2), and each loss is MSE + lam * (1 - S) with S from pair counts."""
+    H, lam = 2, 0.4
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=2, a2=a2, window=W, stripe=St)
+    rng = np.random.default_rng(5 * N + F + d)
+    v = bf16_values((H, g.L, d), rng, -0.4)
+    q, k, vt = (to_device(a[None], torch.bfloat16)
+                for a in (np.zeros((H, g.L, d), np.float32), bf16_values((H, g.L, d), rng), v))
+    rows_np = S.sample_rows(N, F, T, 0.25, 3)
+    modes = torch.empty(H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(H * 8, dtype=torch.float32, device="cuda")
+    ws = svg.alloc_workspace(g, svg.BF16, rows_np.size, svg.MODE_SEARCH)
+    print(f"\n[closed form search N={N} F={F} T={T} d={d}]", flush=True)
+    svg.svg_search_modes(g, q, k, vt, torch.from_numpy(rows_np).cuda(), modes, stats, ws, lam=lam, eps=10.0)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy().reshape(H, 8)
+    L = g.L
+    sparsity = []
+    for c in svg.SEARCH_CANDIDATES:
+        nnz = 0 if c == svg.SKIP else sum(active_keys(g, c, x).size for x in range(L))
+        sparsity.append(1.0 - nnz / L ** 2)
+    for h in range(H):
+        vd = v[h].astype(np.float64)
+        full = np.repeat(vd.mean(axis=0)[None], rows_np.size, axis=0)
+        mse = []
+        for c in svg.SEARCH_CANDIDATES:
+            out = np.stack([vd[active_keys(g, c, x)].mean(axis=0) if c != svg.SKIP else np.zeros(d)
+                            for x in rows_np])
+            mse.append(((out - full) ** 2).mean())
+        want_loss = np.array(mse) + lam * (1.0 - np.array(sparsity))
+        np.testing.assert_allclose(st[h, :4], mse, rtol=1e-3, atol=1e-8, err_msg=f"mse head {h}")
+        np.testing.assert_allclose(st[h, 4:], want_loss, rtol=1e-3, atol=1e-8, err_msg=f"loss head {h}")
