@@ -731,10 +731,21 @@ hipError_t launch_quant_v(const KGeom& g, const void* v, svg_strides s, const in
   return hipGetLastError();
 }
 
+// Waves per workgroup of the FP8 attention kernel, and workgroups per
+// 256-row ranges tile.
+template <bool PV8>
+constexpr int fp8_waves() {
+  return PV8 ? 4 : kAttnWaves;
+}
+template <bool PV8>
+constexpr int fp8_split() {
+  return kBM_bf16 / (32 * fp8_waves<PV8>());
+}
+
 template <int D, bool OUT_BF16, bool PV8>
 static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int64_t grid, int64_t total,
                              hipStream_t st) {
-  constexpr int W = PV8 ? 4 : kAttnWaves;
+  constexpr int W = fp8_waves<PV8>();
   const size_t vtile = PV8 ? (size_t)V8Cfg<D>::TILE_BYTES : (size_t)TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
   const size_t lds = 2 * (size_t)Fp8Cfg<D>::TILE_BYTES + 2 * vtile;
   auto kern = k_attn_fp8<D, OUT_BF16, W, PV8>;
@@ -747,8 +758,7 @@ static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int6
 template <bool PV8>
 static hipError_t launch_fp8_d(const KGeom& g, const Fp8Ptrs& a, bool out_bf16, hipStream_t st) {
   const int32_t nQT = (g.L + kBM_bf16 - 1) / kBM_bf16;
-  // FP8 P.V: two 128-row workgroups per ranges tile
-  const int64_t total = (int64_t)g.B * g.H * nQT * (PV8 ? 2 : 1);
+  const int64_t total = (int64_t)g.B * g.H * nQT * fp8_split<PV8>();
   const int64_t per_round = 8 * kXcdRun;
   const int64_t grid = (total + per_round - 1) / per_round * per_round;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
