@@ -60,6 +60,8 @@ def lib():
         L.og_permute_rows.restype = None
         L.og_row_intervals.argtypes = [g, ctypes.c_int, ctypes.c_int64, vp, vp, ctypes.c_int]
         L.og_row_intervals.restype = ctypes.c_int
+        L.og_max_intervals.argtypes = [g]
+        L.og_max_intervals.restype = ctypes.c_int
         L.og_attention_brute.argtypes = [g, ctypes.c_int, ctypes.c_int32, ctypes.c_double, vp, vp, vp, vp]
         L.og_attention_brute.restype = None
         L.og_attention_rows.argtypes = [g, ctypes.c_int, ctypes.c_int32, ctypes.c_double, vp, vp, vp,
@@ -138,10 +140,21 @@ def permute_rows(g, src, inverse=False):
     return dst
 
 
-def row_intervals(g, mode, x1, max_n=4100):
-    lo = np.zeros(max_n, dtype=np.int64)
-    hi = np.zeros(max_n, dtype=np.int64)
+def max_intervals(g):
+    """Most intervals one row can have (text columns + one per frame)."""
+    return int(lib().og_max_intervals(ctypes.byref(g)))
+
+
+def row_intervals(g, mode, x1, max_n=None):
+    """Active keys of row x1 as [(lo, hi), ...]; raises if more than max_n
+    intervals would be needed (default: enough for any row)."""
+    if max_n is None:
+        max_n = max_intervals(g)
+    lo = np.zeros(max(max_n, 1), dtype=np.int64)
+    hi = np.zeros(max(max_n, 1), dtype=np.int64)
     n = lib().og_row_intervals(ctypes.byref(g), mode, x1, _ptr(lo), _ptr(hi), max_n)
+    if n < 0:
+        raise ValueError(f"row {x1} of mode {mode} needs more than {max_n} intervals")
     return list(zip(lo[:n].tolist(), hi[:n].tolist()))
 
 

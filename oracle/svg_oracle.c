@@ -29,6 +29,7 @@
  * notes and restated at each function below.
  */
 #include <math.h>
+#include <stdio.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -122,6 +123,26 @@ void og_permute_rows(const og_geom* g, int64_t row_bytes, const void* src, void*
 static int64_t mini(int64_t a, int64_t b) { return a < b ? a : b; }
 static int64_t maxi(int64_t a, int64_t b) { return a > b ? a : b; }
 
+/* Largest number of intervals og_row_intervals() can return for this
+ * geometry: the text columns plus one interval per frame (temporal rows). */
+int og_max_intervals(const og_geom* g) { return g->N + 1; }
+
+/* Appends the half-open interval [a, b) to (lo, hi, *n), merging it with the
+ * previous one when they touch.  Returns -1 when the capacity max_n would be
+ * exceeded (nothing is dropped silently). */
+static int push_interval(int64_t a, int64_t b, int64_t* lo, int64_t* hi, int* n, int max_n) {
+  if (b <= a) return 0;
+  if (*n > 0 && hi[*n - 1] == a) {
+    hi[*n - 1] = b;
+    return 0;
+  }
+  if (*n >= max_n) return -1;
+  lo[*n] = a;
+  hi[*n] = b;
+  ++*n;
+  return 0;
+}
+
 /* Active keys of query row x1 as sorted, disjoint, half-open intervals,
  * obtained by solving each predicate of og_mask() for x2:
  *   spatial : floor(u2/F) in [i1-a1+1, i1+a1-1]  -> one interval of frames
@@ -130,84 +151,62 @@ static int64_t maxi(int64_t a, int64_t b) { return a > b ? a : b; }
  *   stripe  : u2 in [0, stripe)
  *   temporal, token-major indices: u2' / N in [j1-a2+1, j1+a2-1]
  * plus the text columns [0, T); a text row sees every key.
- * Returns the number of intervals written (at most max_n). */
+ * Returns the number of intervals written, or -1 when more than max_n would
+ * be needed (og_max_intervals() is always enough). */
 int og_row_intervals(const og_geom* g, int mode, int64_t x1, int64_t* lo, int64_t* hi, int max_n) {
   int64_t T = g->T, N = g->N, F = g->F, L = og_ltot(g);
   int n = 0;
   if (mode == OG_SKIP) return 0;
-  if (x1 < T) {
-    lo[0] = 0;
-    hi[0] = L;
-    return 1;
-  }
+  if (x1 < T) return push_interval(0, L, lo, hi, &n, max_n) < 0 ? -1 : n;
+  if (push_interval(0, T, lo, hi, &n, max_n) < 0) return -1;
   int64_t u1 = x1 - T;
-  /* video-key intervals in u coordinates, appended after the text interval */
-  int64_t vlo[4096], vhi[4096];
-  int nv = 0;
+  int64_t a = 0, b = 0; /* one video interval in u coordinates, unless temporal */
   switch (mode) {
     case OG_SPATIAL: {
       int64_t i1 = u1 / F;
-      vlo[0] = maxi(0, i1 - g->a1 + 1) * F;
-      vhi[0] = mini(N, i1 + g->a1) * F;
-      nv = 1;
+      a = maxi(0, i1 - g->a1 + 1) * F;
+      b = mini(N, i1 + g->a1) * F;
       break;
     }
     case OG_TEMPORAL: {
       int64_t j1 = u1 % F;
       int64_t jl = maxi(0, j1 - g->a2 + 1), jh = mini(F, j1 + g->a2);
-      if (jl == 0 && jh == F) { /* whole frames: one merged interval */
-        vlo[0] = 0;
-        vhi[0] = N * F;
-        nv = 1;
-      } else {
-        for (int64_t i2 = 0; i2 < N && nv < 4096; ++i2) {
-          vlo[nv] = i2 * F + jl;
-          vhi[nv] = i2 * F + jh;
-          ++nv;
-        }
-      }
-      break;
+      for (int64_t i2 = 0; i2 < N; ++i2) /* whole frames merge into one interval */
+        if (push_interval(T + i2 * F + jl, T + i2 * F + jh, lo, hi, &n, max_n) < 0) return -1;
+      return n;
     }
     case OG_TEMPORAL_PERMUTED: {
       int64_t j1 = u1 / N; /* token-major: u' = j*N + i */
-      vlo[0] = maxi(0, j1 - g->a2 + 1) * N;
-      vhi[0] = mini(F, j1 + g->a2) * N;
-      nv = 1;
+      a = maxi(0, j1 - g->a2 + 1) * N;
+      b = mini(F, j1 + g->a2) * N;
       break;
     }
     case OG_FULL:
-      vlo[0] = 0;
-      vhi[0] = N * F;
-      nv = 1;
+      a = 0;
+      b = N * F;
       break;
     case OG_WINDOW:
-      vlo[0] = maxi(0, u1 - g->window + 1);
-      vhi[0] = mini(N * F, u1 + g->window);
-      nv = 1;
+      a = maxi(0, u1 - g->window + 1);
+      b = mini(N * F, u1 + g->window);
       break;
     case OG_STRIPE:
-      vlo[0] = 0;
-      vhi[0] = mini(N * F, g->stripe);
-      nv = 1;
+      a = 0;
+      b = mini(N * F, g->stripe);
       break;
     default:
       return 0;
   }
-  if (T > 0 && n < max_n) {
-    lo[n] = 0;
-    hi[n] = T;
-    ++n;
-  }
-  for (int k = 0; k < nv; ++k) {
-    if (vhi[k] <= vlo[k]) continue;
-    int64_t a = T + vlo[k], b = T + vhi[k];
-    if (n > 0 && hi[n - 1] == a) { /* touching: merge */
-      hi[n - 1] = b;
-    } else if (n < max_n) {
-      lo[n] = a;
-      hi[n] = b;
-      ++n;
-    }
+  if (push_interval(T + a, T + b, lo, hi, &n, max_n) < 0) return -1;
+  return n;
+}
+
+/* og_row_intervals() for the internal callers, whose buffers hold
+ * og_max_intervals() entries: an overflow there is a bug, so it aborts. */
+static int row_intervals_checked(const og_geom* g, int mode, int64_t x1, int64_t* lo, int64_t* hi) {
+  int n = og_row_intervals(g, mode, x1, lo, hi, og_max_intervals(g));
+  if (n < 0) {
+    fprintf(stderr, "svg oracle: interval capacity exceeded (mode %d, row %lld)\n", mode, (long long)x1);
+    abort();
   }
   return n;
 }
@@ -265,11 +264,12 @@ void og_attention_rows(const og_geom* g, int mode, int32_t d, double scale, cons
   {
     int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)L);
     double* sbuf = (double*)malloc(sizeof(double) * (size_t)L);
-    int64_t lo[4100], hi[4100];
+    int64_t* lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
+    int64_t* hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
 #pragma omp for schedule(dynamic, 4)
     for (int64_t r = 0; r < n_rows; ++r) {
       int64_t x1 = rows[r];
-      int ni = og_row_intervals(g, mode, x1, lo, hi, 4100);
+      int ni = row_intervals_checked(g, mode, x1, lo, hi);
       int64_t nk = 0;
       for (int t = 0; t < ni; ++t)
         for (int64_t x2 = lo[t]; x2 < hi[t]; ++x2) keys[nk++] = x2;
@@ -277,6 +277,8 @@ void og_attention_rows(const og_geom* g, int mode, int32_t d, double scale, cons
     }
     free(keys);
     free(sbuf);
+    free(lo);
+    free(hi);
   }
 }
 
@@ -323,11 +325,17 @@ void og_profile_head(const og_geom* g, int32_t d, double scale, const float* q, 
  * counted pair by pair).  SKIP has none. */
 int64_t og_mask_nnz(const og_geom* g, int mode) {
   int64_t L = og_ltot(g), total = 0;
-#pragma omp parallel for reduction(+ : total) schedule(static)
-  for (int64_t x1 = 0; x1 < L; ++x1) {
-    int64_t lo[4100], hi[4100];
-    int ni = og_row_intervals(g, mode, x1, lo, hi, 4100);
-    for (int t = 0; t < ni; ++t) total += hi[t] - lo[t];
+#pragma omp parallel reduction(+ : total)
+  {
+    int64_t* lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
+    int64_t* hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
+#pragma omp for schedule(static)
+    for (int64_t x1 = 0; x1 < L; ++x1) {
+      int ni = row_intervals_checked(g, mode, x1, lo, hi);
+      for (int t = 0; t < ni; ++t) total += hi[t] - lo[t];
+    }
+    free(lo);
+    free(hi);
   }
   return total;
 }
@@ -398,14 +406,20 @@ void og_blocks_rows(const og_geom* g, int mode, int32_t BM, int32_t BN, uint8_t*
   int64_t nq = (L + BM - 1) / BM, nkt = (L + BN - 1) / BN;
   int wm = working_mode(mode);
   memset(bitmap, 0, (size_t)(nq * nkt));
-#pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t qb = 0; qb < nq; ++qb) {
-    int64_t lo[4100], hi[4100];
-    for (int64_t x1 = qb * BM; x1 < mini(L, (qb + 1) * BM); ++x1) {
-      int ni = og_row_intervals(g, wm, x1, lo, hi, 4100);
-      for (int t = 0; t < ni; ++t)
-        for (int64_t kb = lo[t] / BN; kb <= (hi[t] - 1) / BN; ++kb) bitmap[qb * nkt + kb] = 1;
+#pragma omp parallel
+  {
+    int64_t* lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
+    int64_t* hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)og_max_intervals(g));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t qb = 0; qb < nq; ++qb) {
+      for (int64_t x1 = qb * BM; x1 < mini(L, (qb + 1) * BM); ++x1) {
+        int ni = row_intervals_checked(g, wm, x1, lo, hi);
+        for (int t = 0; t < ni; ++t)
+          for (int64_t kb = lo[t] / BN; kb <= (hi[t] - 1) / BN; ++kb) bitmap[qb * nkt + kb] = 1;
+      }
     }
+    free(lo);
+    free(hi);
   }
 }
 

@@ -56,3 +56,12 @@ def sample_check_rows(L, T, extra=(), n=48, seed=0):
     rows = {0, L - 1, max(0, T - 1), T, min(L - 1, T + 1)} | set(int(x) for x in extra if 0 <= x < L)
     rows |= set(rng.choice(L, size=min(n, L), replace=False).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def rows_per_tile(L, BM, seed=0):
+    """One seeded row inside every BM-row query tile (the last tile may be
+    ragged), so a full-size check visits every tile of the kernel's grid."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, L, BM)
+    ends = np.minimum(starts + BM, L)
+    return (starts + (rng.random(starts.size) * (ends - starts)).astype(np.int64)).astype(np.int64)

@@ -1,12 +1,14 @@
 """GPU parity of the whole layer (svg_layer_forward) at the five workload
 shapes, in the launch configuration bench.py times (marked gpu).
 
-Per workload: every head's label equals its planted type (bit-exact) and the
-oracle's label on a subset of heads (bit-exact, statistics within 2 %);
-outputs of every head on sampled rows (first/last rows, band edges, seeded
-picks) within max-abs 2e-2 / RMS 2e-3 (bf16) or 1e-5 (fp32) of the oracle;
-explicit and virtual layout transformation give identical bits; a rerun is
-bit-identical.  Shapes:
+Per workload: every head's label equals its planted type and the oracle's
+label (bit-exact; statistics within 2 %); every head's key-tile ranges, as
+svg_build_blocks lays them out for the kernel's tiles, expand to exactly the
+oracle's tile bitmap, and the head order equals the oracle's longest-first
+order of those bitmaps; outputs of every head on sampled rows (a seeded row in every query
+tile, first/last rows, band edges, seeded picks) within max-abs 2e-2 / RMS 2e-3 (bf16) or
+1e-5 (fp32) of the oracle; explicit and virtual layout transformation give
+identical bits; a rerun is bit-identical.  Shapes:
   0  tiny fp32        4 x 64 tokens, 2 heads, d 64, all rows profiled
   1  CogVideoX-like   13 x 4080, 48 heads, d 64
   2  HunyuanVideo-like 33 x 3600, 24 heads, d 128
@@ -19,7 +21,7 @@ import pytest
 import oracle
 import sparse_attention_video_svg_amd as svg
 import svg_synth as S
-from helpers import check_close, ogeom, sample_check_rows, scale_of
+from helpers import block_bitmap_from_ranges, check_close, ogeom, rows_per_tile, sample_check_rows, scale_of
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -87,27 +89,46 @@ def test_layer_parity(cfg, call):
         assert np.array_equal(lab, inp["kinds"])
     og = ogeom(g)
     sc = scale_of(g)
-    # oracle profile on a subset of heads (one of each label present)
+    # key-tile lists of every head, in the kernel's tiles, against the
+    # oracle's element-level bitmap; head order against the oracle's
+    BM, BN = svg.svg_tile_config(svg.BF16 if bf16 else svg.F32, g.d)
+    nq, nk = -(-g.L // BM), -(-g.L // BN)
+    modes_dev = torch.from_numpy(lab.astype(np.int32)).cuda()
+    ranges = torch.full((g.H * nq * 4,), -1, dtype=torch.int32, device="cuda")
+    order = torch.full((g.H,), -1, dtype=torch.int32, device="cuda")
+    svg.svg_build_blocks(g, modes_dev, BM, BN, ranges, order)
+    torch.cuda.synchronize()
+    rg = ranges.cpu().numpy().reshape(g.H, nq * 4)
+    work = np.zeros(g.H, dtype=np.int64)
+    for h in range(g.H):
+        got = block_bitmap_from_ranges(rg[h], nq, nk)
+        want = oracle.blocks(og, int(lab[h]), BM, BN)
+        assert np.array_equal(got, want), (f"config {cfg} head {h} (mode {lab[h]}): tile lists differ in "
+                                           f"{int((got != want).sum())} of {nq * nk} tiles")
+        work[h] = int(want.sum())
+    assert np.array_equal(order.cpu().numpy(), oracle.head_order(work)), "head order"
+    print(f"  tile lists: {g.H} heads bit-exact ({nq} x {nk} tiles each), head order equal", flush=True)
+    # the oracle's profiling of every head
     if profile:
-        picked = []
-        for want_label in sorted(set(lab.tolist())):
-            picked.append(int(np.nonzero(lab == want_label)[0][0]))
-        if cfg == 0:
-            picked = list(range(g.H))
-        for h in picked:
+        for h in range(g.H):
             ref_label, ref_stats = oracle.profile_head(og, inp["q"][h], inp["k"][h], inp["v"][h], sc,
                                                        inp["rows"].astype(np.int64))
             assert lab[h] == ref_label, (h, lab[h], ref_label)
             np.testing.assert_allclose(st[h], ref_stats, rtol=2e-2, atol=1e-4)
-            print(f"  head {h}: label {lab[h]} stats {st[h]} oracle {ref_stats}", flush=True)
+        print(f"  labels: all {g.H} heads equal the oracle's", flush=True)
     # outputs of every head on sampled rows
     out = o_e[0].float().cpu().numpy()
     worst = (0.0, 0.0)
+    inv = oracle.perm_inv_index(og) if cfg != 0 else None  # token-major row -> natural row
     for h in range(g.H):
         if cfg == 0:
             check = np.arange(g.L)
         else:
-            check = sample_check_rows(g.L, g.T, band_edge_rows(g, lab[h]), n=24, seed=h)
+            # temporal heads run in token-major order: a row in each of those query tiles
+            tiles = rows_per_tile(g.L, BM, seed=h)
+            if lab[h] == svg.TEMPORAL:
+                tiles = inv[tiles]
+            check = np.union1d(sample_check_rows(g.L, g.T, band_edge_rows(g, lab[h]), n=24, seed=h), tiles)
         ref = oracle.attention_rows(og, int(lab[h]), inp["q"][h], inp["k"][h], inp["v"][h], sc, check)
         mx, rms = check_close(out[h][check], ref, "bf16" if bf16 else "f32", what=f"config {cfg} head {h}")
         worst = (max(worst[0], mx), max(worst[1], rms))

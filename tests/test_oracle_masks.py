@@ -196,3 +196,24 @@ def test_row_intervals_match_predicate(oracle_lib, N, F, T):
                     prev = hi
                     got[lo:hi] = 1
                 assert np.array_equal(got, m[x1]), (mode, x1)
+
+
+def test_row_intervals_never_truncate(oracle_lib):
+    """A temporal row with many frames has one interval per frame: more
+    frames than any fixed buffer must still come out whole, and a capacity
+    that is too small is an error, not a silently shortened list."""
+    N, F, T, a2 = 5000, 4, 3, 1
+    g = oracle.geom(N, F, T, 1, a2)
+    assert oracle.max_intervals(g) == N + 1
+    x1 = T + 7 * F + 2  # frame 7, position 2
+    iv = oracle.row_intervals(g, oracle.TEMPORAL, x1)
+    assert len(iv) == N + 1  # the text columns, then position 2 of every frame
+    assert iv[0] == (0, T)
+    assert all(iv[1 + i] == (T + i * F + 2, T + i * F + 3) for i in range(N))
+    with pytest.raises(ValueError):
+        oracle.row_intervals(g, oracle.TEMPORAL, x1, max_n=N)
+    # whole-map count against the closed form N^2 (F + 2 sum_{k<a2} (F-k)) plus the dense text rows/columns
+    g0 = oracle.geom(N, F, 0, 1, a2)
+    assert oracle.mask_nnz(g0, oracle.TEMPORAL) == N * N * F
+    L = T + N * F
+    assert oracle.mask_nnz(g, oracle.TEMPORAL) == N * N * F + T * L + N * F * T
