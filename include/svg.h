@@ -321,6 +321,31 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
                              const int32_t* modes_in, int32_t* labels_out, float* stats_out,
                              int32_t flags, void* ws, size_t ws_bytes, void* stream);
 
+/* svg_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, with the workspace taken from a fixed scratch
+ * array that the library holds on each device it runs on (one per device,
+ * svg_noalloc_scratch_bytes() = 64 MiB, kept until the process ends).  The
+ * layout transformation is always the index-map one (as with
+ * SVG_FLAG_VIRTUAL_PERMUTE; results are bit-identical to the explicit one);
+ * the profiling sweeps use as many key slices as fit in the scratch, so the
+ * statistics can differ from svg_layer_forward's in the last bits of their
+ * fp32 sums, while labels and outputs are the same.  Calls no allocating
+ * routine.  Every call on a device shares that device's scratch: calls that
+ * overlap in time on one device (other streams, other host threads) race and
+ * must be ordered by the caller.  flags: 0 or SVG_FLAG_VIRTUAL_PERMUTE.
+ * Errors: as svg_layer_forward; SVG_E_UNSUPPORTED for the fp8 flags;
+ * SVG_E_WORKSPACE when the layer needs more scratch than the array holds
+ * (before anything is enqueued). */
+svg_status svg_layer_forward_noalloc(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q,
+                                     const void* k, const void* v, svg_strides s, void* o, svg_strides so,
+                                     const int32_t* rows, int32_t n_rows, float fallback_rel_mse,
+                                     const int32_t* modes_in, int32_t* labels_out, float* stats_out,
+                                     int32_t flags, void* stream);
+
+/* Size in bytes of the fixed scratch of svg_layer_forward_noalloc. */
+size_t svg_noalloc_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ __all__ = [
     "FP8_SCORES", "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
     "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
     "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_quantize_v",
-    "svg_sparse_attention_fp8_pv", "FP8_PV", "svg_layer_forward", "library_path",
+    "svg_sparse_attention_fp8_pv", "FP8_PV", "svg_layer_forward", "svg_layer_forward_noalloc",
+    "svg_noalloc_scratch_bytes", "library_path",
     "Svg2Params", "SVG2_INIT_GIVEN", "svg2_workspace_bytes", "svg2_kmeans", "svg2_forward",
 ]
 
@@ -165,6 +166,9 @@ def _lib():
                               ctypes.c_size_t, vp], i32),
             "svg_layer_forward": ([g, i32, i32, vp, vp, vp, S, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp], i32),
+            "svg_layer_forward_noalloc": ([g, i32, i32, vp, vp, vp, S, vp, S, vp, i32, ctypes.c_float, vp, vp, vp,
+                                           i32, vp], i32),
+            "svg_noalloc_scratch_bytes": ([], ctypes.c_size_t),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -461,6 +465,38 @@ def svg_layer_forward(geom, q, k, v, o, ws, rows=None, labels_out=None, stats_ou
         ctypes.byref(g), _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(o),
         _strides(o), _ptr(rows), n_rows, float(fallback_rel_mse), _ptr(modes_in), _ptr(labels_out),
         _ptr(stats_out), flags, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def svg_layer_forward_noalloc(geom, q, k, v, o, rows=None, labels_out=None, stats_out=None, modes_in=None,
+                              fallback_rel_mse=0.05, flags=0, stream=None):
+    """svg_layer_forward without a workspace argument: the library's fixed
+    per-device scratch is used instead (no allocation anywhere in the call;
+    calls that overlap on one device race on that scratch)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_shape(geom, t, name)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k and v must share strides")
+    BH = geom.B * geom.H
+    _check_vec(rows, "rows", _t_i32(), 1, optional=True)
+    _check_vec(modes_in, "modes_in", _t_i32(), BH, optional=True)
+    _check_vec(labels_out, "labels_out", _t_i32(), BH, optional=True)
+    _check_vec(stats_out, "stats_out", _t_f32(), BH * 3, optional=True)
+    if DEBUG:
+        if rows is not None:
+            _debug_rows(geom, rows)
+        if modes_in is not None:
+            _debug_modes(geom, modes_in)
+    g = geom.c()
+    n_rows = 0 if rows is None else rows.numel()
+    _check(_lib().svg_layer_forward_noalloc(
+        ctypes.byref(g), _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(o),
+        _strides(o), _ptr(rows), n_rows, float(fallback_rel_mse), _ptr(modes_in), _ptr(labels_out),
+        _ptr(stats_out), flags, _stream(stream)))
+
+
+def svg_noalloc_scratch_bytes():
+    """Bytes of the fixed per-device scratch of svg_layer_forward_noalloc."""
+    return int(_lib().svg_noalloc_scratch_bytes())
 
 
 def svg2_workspace_bytes(geom, params):

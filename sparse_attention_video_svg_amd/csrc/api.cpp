@@ -93,7 +93,7 @@ svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const ch
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
+int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t ks_cap) {
   // key slices of each profiling sweep.  The full sweep runs one workgroup
   // (rows chunk x head x slice) per CU at a time, so its time goes as
   // ceil(workgroups / CUs) rounds of 1/ks of a chunk's keys each: take the
@@ -105,7 +105,8 @@ int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
   const int64_t chunks = (n_rows + kProfRows_bf16 - 1) / kProfRows_bf16;
   const int64_t wgs = chunks * g.B * g.H;
   const int64_t nkt = (g.L + kBN_bf16 - 1) / kBN_bf16;
-  const int64_t kmax = nkt < 16 ? nkt : 16;
+  int64_t kmax = nkt < 16 ? nkt : 16;
+  kmax = kmax < ks_cap ? kmax : ks_cap;
   int64_t best = 1;
   double best_t = 1e300;
   for (int64_t ks = 1; ks <= kmax; ++ks) {
@@ -121,13 +122,15 @@ int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows) {
 }
 
 // Layout: [profiling partials][labels][ranges][head order][permuted Q,K,V,O].
-WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flags) {
+// ks_cap bounds the key slices of the profiling sweeps (fewer slices, fewer
+// partials: the fixed scratch of svg_layer_forward_noalloc).
+WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flags, int32_t ks_cap = 16) {
   WsLayout w{};
   const int64_t BH = (int64_t)g.B * g.H;
   const int32_t BM = dtype == SVG_BF16 ? kBM_bf16 : kBM_f32;
   const int64_t nQT = (g.L + BM - 1) / BM;
   size_t off = 0;
-  w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows) : 0;
+  w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows, ks_cap) : 0;
   const size_t rows_bh = (size_t)BH * n_rows;
   const size_t nstates = (flags & SVG_FLAG_MODE_SEARCH) ? 4 : 3;  // masks swept per row
   w.part_acc = off;
@@ -198,7 +201,7 @@ svg_status validate_attention(const KGeom& g, svg_dtype in, svg_dtype out, const
                               const void* v, svg_strides s, const void* qp, const void* kp, const void* vp,
                               svg_strides sp, const void* o, svg_strides so, const void* op, svg_strides sop,
                               const int32_t* modes, const int32_t* ranges, const int32_t* order, int32_t BM,
-                              int32_t BN, int32_t flags) {
+                              int32_t BN, int32_t flags, bool check_lists = true) {
   if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
   if (in == SVG_F32 && out != SVG_F32) return fail(SVG_E_UNSUPPORTED, "f32 input requires f32 output");
   if (flags & ~SVG_FLAG_VIRTUAL_PERMUTE) return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
@@ -222,8 +225,10 @@ svg_status validate_attention(const KGeom& g, svg_dtype in, svg_dtype out, const
     TRY(check_strides(sop, g, eo, "op"));
   }
   TRY(check_ptr(modes, "modes", 4));
-  TRY(check_ptr(ranges, "ranges", 16));
-  TRY(check_ptr(order, "head_order", 4));
+  if (check_lists) {  // svg_layer_forward places them in its own workspace
+    TRY(check_ptr(ranges, "ranges", 16));
+    TRY(check_ptr(order, "head_order", 4));
+  }
   return SVG_OK;
 }
 
@@ -370,6 +375,121 @@ svg_status check_svg2_params(const KGeom& g, const svg2_params* prm) {
   if (!(prm->p > 0.f) || !isfinite(prm->p)) return fail(SVG_E_INVALID, "p must be finite and > 0");
   return SVG_OK;
 }
+
+}  // namespace
+
+namespace {
+
+// svg_layer_forward, and with fixed_scratch its allocation-free variant: the
+// workspace is then the device's fixed scratch (ws, ws_bytes unused), the
+// layout transformation is always the index-map one (no permuted copies) and
+// the profiling sweeps take as many key slices as fit in the scratch.
+svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q, const void* k,
+                              const void* v, svg_strides s, void* o, svg_strides so, const int32_t* rows,
+                              int32_t n_rows, float fallback_rel_mse, const int32_t* modes_in, int32_t* labels_out,
+                              float* stats_out, int32_t flags, void* ws, size_t ws_bytes, bool fixed_scratch,
+                              void* stream) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
+  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_FP8_SCORES | SVG_FLAG_FP8_PV))
+    return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & SVG_FLAG_FP8_PV) && !(flags & SVG_FLAG_FP8_SCORES))
+    return fail(SVG_E_INVALID, "SVG_FLAG_FP8_PV needs SVG_FLAG_FP8_SCORES");
+  if (fixed_scratch) {
+    if (flags & (SVG_FLAG_FP8_SCORES | SVG_FLAG_FP8_PV))
+      return fail(SVG_E_UNSUPPORTED, "svg_layer_forward_noalloc: the fp8 paths need more scratch than it holds");
+    flags |= SVG_FLAG_VIRTUAL_PERMUTE;
+  }
+  const bool fp8 = flags & SVG_FLAG_FP8_SCORES;
+  const bool fp8pv = flags & SVG_FLAG_FP8_PV;
+  if (fp8 && in != SVG_BF16) return fail(SVG_E_UNSUPPORTED, "fp8 scores take bf16 inputs");
+  if (fp8) flags |= SVG_FLAG_VIRTUAL_PERMUTE;  // the fp8 path reads temporal heads through the index map
+  const bool profile = modes_in == nullptr;
+  if (profile) {
+    TRY(validate_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out));
+  } else {
+    TRY(check_ptr(modes_in, "modes_in", 4));
+    if (labels_out) TRY(check_ptr(labels_out, "labels_out", 4));
+  }
+  WsLayout w = ws_layout(g, in, profile ? n_rows : 0, flags);
+  if (fixed_scratch) {
+    while (w.total > kStaticScratchBytes && w.ksplit > 1) w = ws_layout(g, in, n_rows, flags, w.ksplit - 1);
+    // (only the profiling partials depend on the slice count)
+    if (w.total > kStaticScratchBytes)
+      return fail(SVG_E_WORKSPACE, "svg_layer_forward_noalloc: this layer needs %zu bytes of scratch, the fixed "
+                  "scratch holds %zu", w.total, kStaticScratchBytes);
+  } else {
+    TRY(check_ptr(ws, "ws", 256));
+    if (ws_bytes < w.total) return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  }
+  int32_t BM, BN;
+  TRY(tile_config_impl(in, g.d, &BM, &BN));
+  const bool virt = flags & SVG_FLAG_VIRTUAL_PERMUTE;
+  const int ei = elt_bytes(in), eo = elt_bytes(out);
+  const svg_strides sp{(int64_t)g.H * g.L * g.d, (int64_t)g.L * g.d, g.d};
+  // workspace pointers (ws is the caller's, 256-byte aligned, or the fixed
+  // scratch, whose address is only taken once every argument has passed)
+  auto perm_at = [&](int t) -> void* { return virt ? nullptr : ws_at<char>(ws, w.perm) + t * w.perm_tensor_bytes; };
+  TRY(validate_attention(g, in, out, q, k, v, s, perm_at(0), perm_at(1), perm_at(2), sp, o, so, perm_at(3), sp,
+                         profile ? labels_out : modes_in, nullptr, nullptr, BM, BN, flags & SVG_FLAG_VIRTUAL_PERMUTE,
+                         false));
+  hipError_t e;
+  if (fixed_scratch) {
+    e = static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward_noalloc (scratch address)");
+  }
+  void *qp = perm_at(0), *kp = perm_at(1), *vp = perm_at(2), *op = perm_at(3);
+  int32_t* ranges = ws_at<int32_t>(ws, w.ranges);
+  int32_t* order = ws_at<int32_t>(ws, w.order);
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t* modes = modes_in;
+  if (profile) {
+    e = run_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out, ws, w, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (profiling)");
+    modes = labels_out;
+  } else if (labels_out && labels_out != modes_in) {
+    e = hipMemcpyAsync(labels_out, modes_in, sizeof(int32_t) * g.B * g.H, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (labels copy)");
+  }
+  e = launch_build_blocks(g, modes, BM, BN, ranges, order, st);
+  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (blocks)");
+  if (fp8) {
+    uint8_t* q8 = ws_at<uint8_t>(ws, w.q8);
+    uint8_t* k8 = ws_at<uint8_t>(ws, w.k8);
+    float* sq = ws_at<float>(ws, w.sq);
+    float* sk = ws_at<float>(ws, w.sk);
+    e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 quantisation)");
+    if (fp8pv) {
+      uint8_t* v8 = ws_at<uint8_t>(ws, w.v8);
+      float* svh = ws_at<float>(ws, w.svh);
+      e = launch_quant_v(g, v, s, modes, v8, svh, st);
+      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 V quantisation)");
+      e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, svh, o, so, out == SVG_BF16, modes, ranges, order, st);
+      return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
+    }
+    e = launch_attention_fp8(g, q8, sq, k8, sk, v, s, o, so, out == SVG_BF16, modes, ranges, order, st);
+    return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
+  }
+  if (!virt) {
+    const void* src[3] = {q, k, v};
+    void* dst[3] = {qp, kp, vp};
+    for (int t = 0; t < 3; ++t) {
+      e = launch_permute(g, ei, src[t], s, dst[t], sp, modes, 0, st);
+      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (permute)");
+    }
+  }
+  AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sp, modes, ranges, order, flags};
+  e = run_attention(g, in, out, a, st);
+  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (attention)");
+  if (!virt) {
+    e = launch_permute(g, eo, op, sp, o, so, modes, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (inverse permute)");
+  }
+  return SVG_OK;
+}
+
 
 }  // namespace
 
@@ -665,88 +785,19 @@ svg_status svg_layer_forward(const svg_geom* geom, svg_dtype in, svg_dtype out, 
                              const void* v, svg_strides s, void* o, svg_strides so, const int32_t* rows,
                              int32_t n_rows, float fallback_rel_mse, const int32_t* modes_in, int32_t* labels_out,
                              float* stats_out, int32_t flags, void* ws, size_t ws_bytes, void* stream) {
-  KGeom g;
-  TRY(check_geom(geom, &g));
-  if (!dtype_ok(in) || !dtype_ok(out)) return fail(SVG_E_INVALID, "unknown dtype");
-  if (flags & ~(SVG_FLAG_VIRTUAL_PERMUTE | SVG_FLAG_FP8_SCORES | SVG_FLAG_FP8_PV))
-    return fail(SVG_E_INVALID, "unknown flags 0x%x", flags);
-  if ((flags & SVG_FLAG_FP8_PV) && !(flags & SVG_FLAG_FP8_SCORES))
-    return fail(SVG_E_INVALID, "SVG_FLAG_FP8_PV needs SVG_FLAG_FP8_SCORES");
-  const bool fp8 = flags & SVG_FLAG_FP8_SCORES;
-  const bool fp8pv = flags & SVG_FLAG_FP8_PV;
-  if (fp8 && in != SVG_BF16) return fail(SVG_E_UNSUPPORTED, "fp8 scores take bf16 inputs");
-  if (fp8) flags |= SVG_FLAG_VIRTUAL_PERMUTE;  // the fp8 path reads temporal heads through the index map
-  const bool profile = modes_in == nullptr;
-  if (profile) {
-    TRY(validate_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out));
-  } else {
-    TRY(check_ptr(modes_in, "modes_in", 4));
-    if (labels_out) TRY(check_ptr(labels_out, "labels_out", 4));
-  }
-  const WsLayout w = ws_layout(g, in, profile ? n_rows : 0, flags);
-  TRY(check_ptr(ws, "ws", 256));
-  if (ws_bytes < w.total) return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
-  int32_t BM, BN;
-  TRY(tile_config_impl(in, g.d, &BM, &BN));
-  const bool virt = flags & SVG_FLAG_VIRTUAL_PERMUTE;
-  const int ei = elt_bytes(in), eo = elt_bytes(out);
-  const svg_strides sp{(int64_t)g.H * g.L * g.d, (int64_t)g.L * g.d, g.d};
-  char* perm = ws_at<char>(ws, w.perm);
-  void* qp = virt ? nullptr : perm;
-  void* kp = virt ? nullptr : perm + w.perm_tensor_bytes;
-  void* vp = virt ? nullptr : perm + 2 * w.perm_tensor_bytes;
-  void* op = virt ? nullptr : perm + 3 * w.perm_tensor_bytes;
-  int32_t* ranges = ws_at<int32_t>(ws, w.ranges);
-  int32_t* order = ws_at<int32_t>(ws, w.order);
-  TRY(validate_attention(g, in, out, q, k, v, s, qp, kp, vp, sp, o, so, op, sp, profile ? labels_out : modes_in,
-                         ranges, order, BM, BN, flags & SVG_FLAG_VIRTUAL_PERMUTE));
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  const int32_t* modes = modes_in;
-  if (profile) {
-    e = run_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out, ws, w, st);
-    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (profiling)");
-    modes = labels_out;
-  } else if (labels_out && labels_out != modes_in) {
-    e = hipMemcpyAsync(labels_out, modes_in, sizeof(int32_t) * g.B * g.H, hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (labels copy)");
-  }
-  e = launch_build_blocks(g, modes, BM, BN, ranges, order, st);
-  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (blocks)");
-  if (fp8) {
-    uint8_t* q8 = ws_at<uint8_t>(ws, w.q8);
-    uint8_t* k8 = ws_at<uint8_t>(ws, w.k8);
-    float* sq = ws_at<float>(ws, w.sq);
-    float* sk = ws_at<float>(ws, w.sk);
-    e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, st);
-    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 quantisation)");
-    if (fp8pv) {
-      uint8_t* v8 = ws_at<uint8_t>(ws, w.v8);
-      float* svh = ws_at<float>(ws, w.svh);
-      e = launch_quant_v(g, v, s, modes, v8, svh, st);
-      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (fp8 V quantisation)");
-      e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, svh, o, so, out == SVG_BF16, modes, ranges, order, st);
-      return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
-    }
-    e = launch_attention_fp8(g, q8, sq, k8, sk, v, s, o, so, out == SVG_BF16, modes, ranges, order, st);
-    return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
-  }
-  if (!virt) {
-    const void* src[3] = {q, k, v};
-    void* dst[3] = {qp, kp, vp};
-    for (int t = 0; t < 3; ++t) {
-      e = launch_permute(g, ei, src[t], s, dst[t], sp, modes, 0, st);
-      if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (permute)");
-    }
-  }
-  AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sp, modes, ranges, order, flags};
-  e = run_attention(g, in, out, a, st);
-  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (attention)");
-  if (!virt) {
-    e = launch_permute(g, eo, op, sp, o, so, modes, 1, st);
-    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (inverse permute)");
-  }
-  return SVG_OK;
+  return layer_forward_impl(geom, in, out, q, k, v, s, o, so, rows, n_rows, fallback_rel_mse, modes_in, labels_out,
+                            stats_out, flags, ws, ws_bytes, false, stream);
 }
+
+svg_status svg_layer_forward_noalloc(const svg_geom* geom, svg_dtype in, svg_dtype out, const void* q,
+                                     const void* k, const void* v, svg_strides s, void* o, svg_strides so,
+                                     const int32_t* rows, int32_t n_rows, float fallback_rel_mse,
+                                     const int32_t* modes_in, int32_t* labels_out, float* stats_out, int32_t flags,
+                                     void* stream) {
+  return layer_forward_impl(geom, in, out, q, k, v, s, o, so, rows, n_rows, fallback_rel_mse, modes_in, labels_out,
+                            stats_out, flags, nullptr, 0, true, stream);
+}
+
+size_t svg_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 }  // extern "C"

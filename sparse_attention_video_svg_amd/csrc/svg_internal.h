@@ -162,4 +162,10 @@ constexpr int32_t kBM_f32 = 64, kBN_f32 = 64;
 // Query rows per workgroup of the bf16 profiling sweeps.
 constexpr int32_t kProfRows_bf16 = kBM_bf16;
 
+// Fixed device scratch of svg_layer_forward_noalloc (one array per device,
+// held until the process ends) and its device address on the current device
+// (taken with hipGetSymbolAddress on the first call there).
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+hipError_t static_scratch(void** ptr);
+
 }  // namespace svg

@@ -269,3 +269,25 @@ def test_fp8_pv_validation():
     b = svg.svg_workspace_bytes(gg, svg.BF16, 16, svg.FP8_SCORES | svg.FP8_PV)
     nkt = -(-gg.L // 64)
     assert b - a >= gg.H * nkt * gg.d * 64
+
+
+def test_noalloc_layer_validation():
+    """svg_layer_forward_noalloc rejects on the host, before any HIP call: fp8
+    flags, a layer whose workspace exceeds the fixed scratch even with one key
+    slice, and the same argument errors as svg_layer_forward."""
+    L = raw()
+    s = strides()
+    g = geom().c()
+    assert svg.svg_noalloc_scratch_bytes() == 64 << 20
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A,
+                                       svg.FP8_SCORES, None) == E_UNSUPPORTED
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, None,
+                                       A, 0, None) == E_INVALID
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, None, A, A, s, A, s, A, 8, 0.05, None, A,
+                                       A, 0, None) == E_INVALID
+    # 64 heads x 2048 tokens, all rows profiled: partials 64*2048*3*66*4 bytes > 64 MiB at one slice
+    big = svg.Geom(B=1, H=64, d=64, N=2, F=1024, T=0, a1=1, a2=4, window=64, stripe=64).c()
+    sb = svg._Strides(64 * 2048 * 64, 2048 * 64, 64)
+    assert L.svg_layer_forward_noalloc(ctypes.byref(big), svg.BF16, svg.BF16, A, A, A, sb, A, sb, A, 2048, 0.05, None,
+                                       A, A, 0, None) == E_WORKSPACE
+    assert "scratch" in svg.svg_last_error()
