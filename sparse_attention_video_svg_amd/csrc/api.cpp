@@ -66,6 +66,8 @@ svg_status check_geom(const svg_geom* geom, KGeom* out) {
     k.scale_log2 = (float)((double)k.scale * 1.4426950408889634);
     fastdiv_init((uint32_t)g.N, &k.divN_mul, &k.divN_shift);
     fastdiv_init((uint32_t)g.F, &k.divF_mul, &k.divF_shift);
+    k.nxcd = 8;  // until apply_topology reads the device's own
+    k.ncu = 256;
   }
   return SVG_OK;
 }
@@ -85,6 +87,42 @@ svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const ch
   return SVG_OK;
 }
 
+// Device topology, cached per device id (read once with that device current).
+hipError_t query_topology(DevTopo* t) {
+  static std::atomic<int64_t> cache[64];  // cus << 32 | xcds, 0 = not read yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int64_t c = cache[dev].load(std::memory_order_acquire);
+    if (c != 0) {
+      t->cus = (int32_t)(c >> 32);
+      t->xcds = (int32_t)(c & 0xffffffff);
+      return hipSuccess;
+    }
+  }
+  int cus = 0, xcds = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev);
+  if (e != hipSuccess) return e;
+  t->cus = cus > 0 ? cus : 1;
+  t->xcds = xcds > 0 ? xcds : 1;
+  if (dev >= 0 && dev < 64)
+    cache[dev].store(((int64_t)t->cus << 32) | (int64_t)t->xcds, std::memory_order_release);
+  return hipSuccess;
+}
+
+// The device's CU and XCD counts into g (after every argument has passed).
+hipError_t apply_topology(KGeom* g) {
+  DevTopo t;
+  hipError_t e = query_topology(&t);
+  if (e != hipSuccess) return e;
+  g->ncu = t.cus;
+  g->nxcd = t.xcds;
+  return hipSuccess;
+}
+
 #define TRY(expr)                      \
   do {                                 \
     svg_status _st = (expr);           \
@@ -93,32 +131,17 @@ svg_status check_strides(const svg_strides& s, const KGeom& g, int elt, const ch
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int32_t choose_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t ks_cap) {
-  // key slices of each profiling sweep.  The full sweep runs one workgroup
-  // (rows chunk x head x slice) per CU at a time, so its time goes as
-  // ceil(workgroups / CUs) rounds of 1/ks of a chunk's keys each: take the
-  // ks in 1..16 (and at most the key tiles) that minimises rounds / ks; on
-  // ties the one whose workgroup count is nearest four per CU (enough to
-  // even out chunks of unequal size, few partials to merge).
+// Key slices of the profiling sweeps for `cus` compute units (at most cap).
+// The workspace is laid out for the slices chosen at kRefCUs, the MI355X's
+// 256; a call then takes the slices chosen for the device's own CU count,
+// at most as many as the layout holds.
+constexpr int64_t kRefCUs = 256;
+
+int32_t profile_ksplit(const KGeom& g, svg_dtype dtype, int32_t n_rows, int64_t cus, int32_t cap) {
   if (dtype != SVG_BF16) return 1;
-  constexpr int64_t kCUs = 256;  // MI355X
   const int64_t chunks = (n_rows + kProfRows_bf16 - 1) / kProfRows_bf16;
-  const int64_t wgs = chunks * g.B * g.H;
   const int64_t nkt = (g.L + kBN_bf16 - 1) / kBN_bf16;
-  int64_t kmax = nkt < 16 ? nkt : 16;
-  kmax = kmax < ks_cap ? kmax : ks_cap;
-  int64_t best = 1;
-  double best_t = 1e300;
-  for (int64_t ks = 1; ks <= kmax; ++ks) {
-    const double t = (double)((wgs * ks + kCUs - 1) / kCUs) / (double)ks;
-    const int64_t dist = wgs * ks > 4 * kCUs ? wgs * ks - 4 * kCUs : 4 * kCUs - wgs * ks;
-    const int64_t best_dist = wgs * best > 4 * kCUs ? wgs * best - 4 * kCUs : 4 * kCUs - wgs * best;
-    if (t < best_t - 1e-12 || (t < best_t + 1e-12 && dist < best_dist)) {
-      best_t = t;
-      best = ks;
-    }
-  }
-  return (int32_t)best;
+  return choose_ksplit(chunks * g.B * g.H, nkt, cus, cap);
 }
 
 // Layout: [profiling partials][labels][ranges][head order][permuted Q,K,V,O].
@@ -130,7 +153,7 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
   const int32_t BM = dtype == SVG_BF16 ? kBM_bf16 : kBM_f32;
   const int64_t nQT = (g.L + BM - 1) / BM;
   size_t off = 0;
-  w.ksplit = n_rows > 0 ? choose_ksplit(g, dtype, n_rows, ks_cap) : 0;
+  w.ksplit = n_rows > 0 ? profile_ksplit(g, dtype, n_rows, kRefCUs, ks_cap) : 0;
   const size_t rows_bh = (size_t)BH * n_rows;
   const size_t nstates = (flags & SVG_FLAG_MODE_SEARCH) ? 4 : 3;  // masks swept per row
   w.part_acc = off;
@@ -260,6 +283,8 @@ hipError_t run_profile(const KGeom& g, svg_dtype dtype, const void* q, const voi
                        float* stats, void* ws, const WsLayout& w, hipStream_t st) {
   float* pa = ws_at<float>(ws, w.part_acc);
   float* pm = ws_at<float>(ws, w.part_ml);
+  // key slices for this device's CUs, within the ones the partials hold
+  const int32_t ks = dtype == SVG_BF16 ? profile_ksplit(g, dtype, n_rows, g.ncu, w.ksplit) : w.ksplit;
   hipError_t e;
   if (dtype == SVG_BF16) {
     int32_t* ox = ws_at<int32_t>(ws, w.ord_x);
@@ -267,13 +292,12 @@ hipError_t run_profile(const KGeom& g, svg_dtype dtype, const void* q, const voi
     e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
     if (e != hipSuccess) return e;
     static const int32_t masks[3] = {SVG_SPATIAL, SVG_FULL, SVG_TEMPORAL};  // states 0, 1 (reference), 2
-    e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, masks, 3, pa, pm, st);
+    e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, ks, ox, orr, masks, 3, pa, pm, st);
   } else {
     e = launch_profile_f32(g, q, k, v, s, rows, n_rows, pa, pm, st);
   }
   if (e != hipSuccess) return e;
-  return launch_profile_merge(g, n_rows, w.ksplit, pa, pm, ws_at<double>(ws, w.row_sums), fallback, labels, stats,
-                              st);
+  return launch_profile_merge(g, n_rows, ks, pa, pm, ws_at<double>(ws, w.row_sums), fallback, labels, stats, st);
 }
 
 // Active (query, key) pairs of a mode over the whole L x L map, from the
@@ -434,7 +458,8 @@ svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out,
   TRY(validate_attention(g, in, out, q, k, v, s, perm_at(0), perm_at(1), perm_at(2), sp, o, so, perm_at(3), sp,
                          profile ? labels_out : modes_in, nullptr, nullptr, BM, BN, flags & SVG_FLAG_VIRTUAL_PERMUTE,
                          false));
-  hipError_t e;
+  hipError_t e = apply_topology(&g);
+  if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (device topology)");
   if (fixed_scratch) {
     e = static_scratch(&ws);
     if (e != hipSuccess) return hip_fail(e, "svg_layer_forward_noalloc (scratch address)");
@@ -550,10 +575,12 @@ svg_status svg_search_modes(const svg_geom* geom, svg_dtype dtype, const void* q
   int32_t* ox = ws_at<int32_t>(ws, w.ord_x);
   int32_t* orr = ws_at<int32_t>(ws, w.ord_r);
   static const int32_t masks[4] = {SVG_FULL, SVG_WINDOW, SVG_TEMPORAL, SVG_STRIPE};  // state 0 = reference
-  hipError_t e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
-  if (e == hipSuccess) e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, w.ksplit, ox, orr, masks, 4, pa, pm, st);
+  hipError_t e = apply_topology(&g);
+  const int32_t ks = profile_ksplit(g, dtype, n_rows, g.ncu, w.ksplit);
+  if (e == hipSuccess) e = launch_profile_rank(g, rows, n_rows, ox, orr, st);
+  if (e == hipSuccess) e = launch_sample_sweeps(g, q, k, v, s, rows, n_rows, ks, ox, orr, masks, 4, pa, pm, st);
   if (e == hipSuccess)
-    e = launch_search_merge(g, n_rows, w.ksplit, pa, pm, ws_at<double>(ws, w.row_sums), p, modes_out, stats_out, st);
+    e = launch_search_merge(g, n_rows, ks, pa, pm, ws_at<double>(ws, w.row_sums), p, modes_out, stats_out, st);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_search_modes");
 }
 
@@ -567,7 +594,9 @@ svg_status svg_profile_heads(const svg_geom* geom, svg_dtype dtype, const void* 
   TRY(check_ptr(ws, "ws", 256));
   if (ws_bytes < profile_ws_bytes(w))
     return fail(SVG_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, profile_ws_bytes(w));
-  hipError_t e = run_profile(g, dtype, q, k, v, s, rows, n_rows, fallback_rel_mse, labels, stats, ws, w,
+  hipError_t e = apply_topology(&g);
+  if (e != hipSuccess) return hip_fail(e, "svg_profile_heads (device topology)");
+  e = run_profile(g, dtype, q, k, v, s, rows, n_rows, fallback_rel_mse, labels, stats, ws, w,
                              (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_profile_heads");
 }
@@ -611,7 +640,8 @@ svg_status svg_sparse_attention(const svg_geom* geom, svg_dtype in, svg_dtype ou
   TRY(validate_attention(g, in, out, q, k, v, s, qp, kp, vp, sp, o, so, op, sop, modes, ranges, head_order, BM,
                          BN, flags));
   AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sop, modes, ranges, head_order, flags};
-  hipError_t e = run_attention(g, in, out, a, (hipStream_t)stream);
+  hipError_t e = apply_topology(&g);
+  if (e == hipSuccess) e = run_attention(g, in, out, a, (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention");
 }
 
@@ -653,7 +683,9 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(ranges, "ranges", 16));
   TRY(check_ptr(head_order, "head_order", 4));
-  hipError_t e = launch_attention_fp8(g, q8, sq, k8, sk, v, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
+  hipError_t e = apply_topology(&g);
+  if (e == hipSuccess)
+    e = launch_attention_fp8(g, q8, sq, k8, sk, v, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
                                       (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8");
 }
@@ -693,7 +725,9 @@ svg_status svg_sparse_attention_fp8_pv(const svg_geom* geom, svg_dtype out, cons
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(ranges, "ranges", 16));
   TRY(check_ptr(head_order, "head_order", 4));
-  hipError_t e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
+  hipError_t e = apply_topology(&g);
+  if (e == hipSuccess)
+    e = launch_attention_fp8pv(g, q8, sq, k8, sk, v8, sv, o, so, out == SVG_BF16, modes, ranges, head_order,
                                         (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_sparse_attention_fp8_pv");
 }
@@ -761,7 +795,7 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* prm, svg_dtype 
   int32_t* start_q = ws_at<int32_t>(ws, w.start_q);
   int32_t* start_k = ws_at<int32_t>(ws, w.start_k);
   uint8_t* sel_w = sel ? sel : ws_at<uint8_t>(ws, w.sel);
-  hipError_t e = hipSuccess;
+  hipError_t e = apply_topology(&g);
   if (!(flags & SVG2_FLAG_INIT_GIVEN)) {
     e = launch_km_init(g, q, s, prm->C_q, mu_q, st);
     if (e == hipSuccess) e = launch_km_init(g, k, s, prm->C_k, mu_k, st);

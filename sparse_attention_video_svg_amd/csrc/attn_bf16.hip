@@ -27,10 +27,10 @@
 //    the first tile.  Element masks are evaluated only on tiles that are not
 //    entirely inside every row's run; tiles no row of a wave needs are skipped
 //    by that wave.
-//  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
-//    the 8 XCDs) walks runs of consecutive query tiles of one head, which
-//    share their K/V band in that XCD's L2; runs are handed out in the
-//    longest-head-first order of svg_build_blocks.
+//  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
+//    to the device's XCDs, eight on an MI355X) walks runs of consecutive query
+//    tiles of one head, which share their K/V band in that XCD's L2; runs are
+//    handed out in the longest-head-first order of svg_build_blocks.
 #include "attn_common.h"
 
 namespace svg {
@@ -108,8 +108,7 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 4 : WAVES <= 6 ? 2 : 1)) voi
 
   // XCD-aware remap of the workgroup id, then longest-head-first order.
   const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  const int logical = xcd_logical(w, g.nxcd, kXcdRun);
   if (logical >= total) return;
   const int bh = a.order[logical / nQT];
   const int qt = logical % nQT;
@@ -185,8 +184,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  const int logical = xcd_logical(w, g.nxcd, kXcdRun);
   if (logical >= total) return;
   const int chunks = (n_rows + BMW - 1) / BMW;
   const int chunk = logical % chunks;
@@ -262,8 +260,7 @@ static hipError_t launch_attn(const KGeom& g, const AttnPtrs& a, int32_t nQT, in
 hipError_t launch_attention_bf16(const KGeom& g, const AttnPtrs& a, bool out_bf16, hipStream_t st) {
   const int32_t nQT = (g.L + kBM_bf16 - 1) / kBM_bf16;
   const int64_t total = (int64_t)g.B * g.H * nQT;
-  const int64_t per_round = 8 * kXcdRun;
-  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  const int64_t grid = xcd_grid(total, g.nxcd, kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (g.d == 64)
     return out_bf16 ? launch_attn<64, true>(g, a, nQT, grid, total, st) : launch_attn<64, false>(g, a, nQT, grid, total, st);
@@ -281,8 +278,7 @@ static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, 
   if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
   const int64_t chunks = (n_rows + 32 * W - 1) / (32 * W);
   const int64_t total = chunks * nsplit * g.B * g.H;
-  const int64_t per_round = 8 * kXcdRun;
-  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  const int64_t grid = xcd_grid(total, g.nxcd, kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, q, k, v, s, rows, ord_r, n_rows, nsplit,
                      (int32_t)total, mode, state, nstates, acc, ml);

@@ -666,8 +666,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 3 : 1) void k_attn_fp8(KGe
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  const int logical = xcd_logical(w, g.nxcd, kXcdRun);
   if (logical >= total) return;
   const int bh = a.order[logical / (nQT * SPLIT)];
   const int qt = logical % (nQT * SPLIT), rq = qt / SPLIT;
@@ -759,8 +758,7 @@ template <bool PV8>
 static hipError_t launch_fp8_d(const KGeom& g, const Fp8Ptrs& a, bool out_bf16, hipStream_t st) {
   const int32_t nQT = (g.L + kBM_bf16 - 1) / kBM_bf16;
   const int64_t total = (int64_t)g.B * g.H * nQT * fp8_split<PV8>();
-  const int64_t per_round = 8 * kXcdRun;
-  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  const int64_t grid = xcd_grid(total, g.nxcd, kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (g.d == 64)
     return out_bf16 ? launch_fp8<64, true, PV8>(g, a, nQT, grid, total, st)

@@ -14,11 +14,12 @@
 namespace svg {
 
 constexpr int kTI = 8, kTJ = 8;  // frames x positions per workgroup
+constexpr int kPermThreads = 256;
 typedef int i32x4n __attribute__((ext_vector_type(4)));
 
 // One workgroup moves up to 64 rows of RB bytes (RB = d * element size).
 template <int RB>
-__global__ __launch_bounds__(256) void k_permute(KGeom g, const char* __restrict__ src, svg_strides ss,
+__global__ __launch_bounds__(kPermThreads) void k_permute(KGeom g, const char* __restrict__ src, svg_strides ss,
                                                  char* __restrict__ dst, svg_strides ds, int elt,
                                                  const int32_t* __restrict__ modes, int inverse,
                                                  int nbi, int nbj, int ntext) {
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void k_permute(KGeom g, const char* __restrict
   int blk = blockIdx.x;
   if (blk < ntext) {  // text rows: plain copy of up to 64 rows
     const int r0 = blk * 64;
-    for (int c = t; c < 64 * CPR; c += 256) {
+    for (int c = t; c < 64 * CPR; c += kPermThreads) {
       const int r = r0 + c / CPR;
       if (r < g.T) {
         const int4 val = *reinterpret_cast<const int4*>(sbase + r * srow + (c % CPR) * 16);
@@ -44,11 +45,14 @@ __global__ __launch_bounds__(256) void k_permute(KGeom g, const char* __restrict
     return;
   }
   blk -= ntext;
-  const int i0 = (blk / nbj) * kTI, j0 = (blk % nbj) * kTJ;
+  // consecutive workgroups take consecutive frame blocks of one position
+  // block, so those writing one token-major region (every frame of eight
+  // positions) run together (+11 % forward against position blocks first)
+  const int i0 = (blk % nbi) * kTI, j0 = (blk / nbi) * kTJ;
   // forward: read runs along j (frame-major rows i*F + j), write runs along i
   // inverse: read runs along i (token-major rows j*N + i), write runs along j
   // (the source is read once: non-temporal loads, +5 % on the forward pass)
-  for (int c = t; c < kTI * kTJ * CPR; c += 256) {
+  for (int c = t; c < kTI * kTJ * CPR; c += kPermThreads) {
     const int rr = c / CPR, ch = c % CPR;
     int a, bb;  // a: frame offset, bb: position offset
     if (!inverse) {
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256) void k_permute(KGeom g, const char* __restrict
     }
   }
   __syncthreads();
-  for (int c = t; c < kTI * kTJ * CPR; c += 256) {
+  for (int c = t; c < kTI * kTJ * CPR; c += kPermThreads) {
     const int rr = c / CPR, ch = c % CPR;
     int a, bb;
     if (!inverse) {
@@ -94,15 +98,15 @@ hipError_t launch_permute(const KGeom& g, int elt, const void* src, svg_strides 
   char* d = static_cast<char*>(dst);
   switch (rb) {
     case 128:
-      hipLaunchKernelGGL(k_permute<128>, grid, dim3(256), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
+      hipLaunchKernelGGL(k_permute<128>, grid, dim3(kPermThreads), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
                          nbj, ntext);
       break;
     case 256:
-      hipLaunchKernelGGL(k_permute<256>, grid, dim3(256), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
+      hipLaunchKernelGGL(k_permute<256>, grid, dim3(kPermThreads), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
                          nbj, ntext);
       break;
     case 512:
-      hipLaunchKernelGGL(k_permute<512>, grid, dim3(256), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
+      hipLaunchKernelGGL(k_permute<512>, grid, dim3(kPermThreads), 0, st, g, s, ss, d, ds, elt, modes, inverse, nbi,
                          nbj, ntext);
       break;
     default:

@@ -538,8 +538,7 @@ __global__ __launch_bounds__(512, 1) void k_svg2_attn(KGeom g, Svg2Ptrs a) {
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int logical = ((slot / kXcdRun) * 8 + xcd) * kXcdRun + (slot % kXcdRun);
+  const int logical = xcd_logical(w, g.nxcd, kXcdRun);
   if (logical >= a.total) return;
   const int bh = logical / a.max_rb, j = logical % a.max_rb;
   const int32_t* rbp = a.rb_prefix + (int64_t)bh * (a.Cq + 1);
@@ -715,8 +714,7 @@ hipError_t launch_svg2_attention(const KGeom& g, const void* q, svg_strides s, c
   a.Ck = Ck;
   a.max_rb = (g.L + 255) / 256 + Cq;  // sum over clusters of ceil(n_a / 256) is below this
   const int64_t total = (int64_t)g.B * g.H * a.max_rb;
-  const int64_t per_round = 8 * kXcdRun;
-  const int64_t grid = (total + per_round - 1) / per_round * per_round;
+  const int64_t grid = xcd_grid(total, g.nxcd, kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   a.total = (int32_t)total;
   if (g.d == 64)

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "svg.h"
+#include "svg_sched.h"
 #include <atomic>
 
 namespace svg {
@@ -18,7 +19,16 @@ struct KGeom {
   float scale_log2;   // scale * log2(e)
   // invariant-divisor constants for x/N and x/F (see FastDiv)
   uint32_t divN_mul, divN_shift, divF_mul, divF_shift;
+  int32_t nxcd;       // XCDs of the device the kernels run on (>= 1)
+  int32_t ncu;        // its compute units
 };
+
+// Compute units and XCDs of the current device, read from the runtime once
+// per device (a partitioned or CU-masked device reports its own share).
+struct DevTopo {
+  int32_t cus, xcds;
+};
+hipError_t device_topology(DevTopo* t);
 
 // Division of a non-negative int32 by an invariant positive divisor with one
 // multiply-high, after Granlund and Montgomery, "Division by invariant
@@ -45,7 +55,7 @@ struct WsLayout {
   size_t q8, k8, sq, sk;     // fp8-score path: quantised Q, K and their scales
   size_t v8, svh;            // fp8 P.V: quantised V tiles and per-head scales
   size_t perm_tensor_bytes;  // one permuted tensor (all heads)
-  int32_t ksplit;            // key splits of the profiling sweep
+  int32_t ksplit;            // key slices the profiling partials are laid out for
 };
 
 // Launchers (each returns hipGetLastError() after its launches).
