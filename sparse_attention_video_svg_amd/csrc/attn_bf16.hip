@@ -73,13 +73,19 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
   const float l_tot = half_sum(st.l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (valid) {
-    char* orow = O + (obase + (int64_t)phys(xq) * sout.x) * OE;
+  // the output row and column offset are formed anew from the lane id here
+  // (read in asm so that it is not shared with the one taken before the
+  // sweep), so that nothing of them stays live across the key loop
+  int lid;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+  const int xo = qt * BMW + wave * 32 + (lid & 31), ho = lid >> 5;
+  if (xo < g.L) {
+    char* orow = O + (obase + (int64_t)phys(xo) * sout.x) * OE;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hh;
+        const int d0 = db * 32 + 8 * g4 + 4 * ho;
         f32x4 v4 = {st.o[db][4 * g4] * inv, st.o[db][4 * g4 + 1] * inv, st.o[db][4 * g4 + 2] * inv,
                     st.o[db][4 * g4 + 3] * inv};
         if (OUT_BF16) {

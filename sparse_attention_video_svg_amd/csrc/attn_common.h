@@ -129,7 +129,8 @@ __device__ __forceinline__ f32x16 score_block(const __bf16* lds_k, const bf16x8*
 template <int D, bool ACC = false>
 __device__ __forceinline__ void score_tile(const __bf16* lds_k, const bf16x8* qf, int lane, f32x16& s0, f32x16& s1) {
   using C = TileCfg<D>;
-  constexpr int KS = D / 16, kAhead = 3;
+  // (d 64 has four steps and a 128-register budget: one step ahead)
+  constexpr int KS = D / 16, kAhead = D == 64 ? 1 : 3;
   const int hh = lane >> 5;
   const int m0 = lane & 31, m1 = 32 + (lane & 31);
   const int sw0 = C::swz_k(m0), sw1 = C::swz_k(m1);
@@ -193,6 +194,15 @@ __device__ __forceinline__ int acc_key(int kb2, int r, int hh) {
   return kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+// Max of a lane's scores over both 32-key blocks of a tile (its row: the
+// lane and its partner lane^32 hold the two halves), in log2 units.
+__device__ __forceinline__ float tile_max(const f32x16& s0, const f32x16& s1, float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  return half_max(mx) * sl2;
+}
+
 // Online-softmax state of one output (per lane: one query, the dims of the
 // accumulator layout).  m_ref is the running reference max in log2 units; it
 // only moves when a lane's tile max exceeds it by more than 2^kRescaleTau, and
@@ -210,15 +220,11 @@ struct Flash {
     l_part = 0.f;
   }
 
-  // s0, s1: raw scores of the two 32-key blocks of a tile, masked entries
-  // already -inf.  sl2 = scale * log2(e) > 0.  Leaves the tile's weights as
-  // bf16 in pbs (key step s16 = 16 keys each) and folds their row sum into
-  // l_part; rescales o when the reference max moves.
-  __device__ __forceinline__ void softmax(const f32x16& s0, const f32x16& s1, float sl2, bf16x8* pbs) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = half_max(mx) * sl2;
+  // Moves the reference max to mx (the tile's max in log2 units) on lanes
+  // where it exceeds the reference by more than 2^kRescaleTau, rescaling o
+  // and l_part there; a wave-uniform branch, almost never taken after the
+  // first tile.
+  __device__ __forceinline__ void rescale(float mx) {
     const bool need = mx > m_ref + kRescaleTau;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       // lanes with nothing accumulated yet (m_ref = -inf) hold o = l = 0
@@ -228,26 +234,38 @@ struct Flash {
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m_ref = need ? mx : m_ref;
     }
-    const float nmu = m_ref == -INFINITY ? 0.f : -m_ref;
+  }
+
+  // The weights 2^(s * sl2 - m_ref) of key step s16 (16 keys) as bf16, their
+  // row sum folded into l_part.
+  __device__ __forceinline__ bf16x8 weights(const f32x16& s0, const f32x16& s1, float sl2, float nmu, int s16) {
+    f32x8 p8;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float sv = (s16 >> 1) ? s1[(s16 & 1) * 8 + r] : s0[(s16 & 1) * 8 + r];
+      p8[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sl2, nmu));
+    }
+    const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+    // row sum of the bf16 weights the P.V product actually uses, two per
+    // v_dot2_f32_bf16 against (1, 1)
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int s16 = 0; s16 < 4; ++s16) {
-      f32x8 p8;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float sv = (s16 >> 1) ? s1[(s16 & 1) * 8 + r] : s0[(s16 & 1) * 8 + r];
-        p8[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sl2, nmu));
-      }
-      const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
-      // row sum of the bf16 weights the P.V product actually uses, two per
-      // v_dot2_f32_bf16 against (1, 1)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part, false);
-      }
-      pbs[s16] = pb;
+    for (int r = 0; r < 4; ++r) {
+      const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part, false);
     }
+    return pb;
+  }
+
+  // s0, s1: raw scores of the two 32-key blocks of a tile, masked entries
+  // already -inf.  sl2 = scale * log2(e) > 0.  Leaves the tile's weights as
+  // bf16 in pbs (key step s16 = 16 keys each) and folds their row sum into
+  // l_part; rescales o when the reference max moves.
+  __device__ __forceinline__ void softmax(const f32x16& s0, const f32x16& s1, float sl2, bf16x8* pbs) {
+    rescale(tile_max(s0, s1, sl2));
+    const float nmu = m_ref == -INFINITY ? 0.f : -m_ref;
+#pragma unroll
+    for (int s16 = 0; s16 < 4; ++s16) pbs[s16] = weights(s0, s1, sl2, nmu, s16);
   }
 
   // o += P V for the weights of one tile; V^T fragments read from LDS.
