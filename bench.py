@@ -68,38 +68,64 @@ def pair_count(N, F, T, mode, a1=1, a2=1, window=1, stripe=1):
     return text + vid
 
 
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_attn_bf16_hunyuanvideo_33x3600_h24_d128.md")
-# the bf16 attention kernel's source: its file and the headers it is built from
-ATTN_SOURCES = [os.path.join(ROOT, "sparse_attention_video_svg_amd", "csrc", f)
-                for f in ("attn_bf16.hip", "attn_common.h", "svg_device.h", "svg_internal.h")]
+CSRC = os.path.join(ROOT, "sparse_attention_video_svg_amd", "csrc")
+# the sources each timed kernel is built from: a committed counter record is
+# used only while the hash of its kernel's sources is the one it was taken at
+KERNEL_SOURCES = {
+    "k_attn_bf16": ("attn_bf16.hip", "attn_common.h", "svg_device.h", "svg_internal.h", "svg_sched.h"),
+    "k_attn_fp8": ("attn_fp8.hip", "attn_common.h", "svg_device.h", "svg_internal.h", "svg_sched.h"),
+    "k_svg2_attn": ("svg2.hip", "attn_common.h", "svg_device.h", "svg_internal.h", "svg_sched.h"),
+    "k_permute": ("permute.hip", "svg_device.h", "svg_internal.h"),
+}
+# rocprofv3 summaries under profiles/ holding an HBM-traffic record, by
+# (timed kernel, workload, layout)
+TRAFFIC_RECORDS = {
+    ("k_attn_bf16", 1, "explicit"): "k_attn_bf16_cogvideox_13x4080_h48_d64.md",
+    ("k_attn_bf16", 2, "explicit"): "k_attn_bf16_hunyuanvideo_33x3600_h24_d128.md",
+    ("k_attn_bf16", 3, "explicit"): "k_attn_bf16_hunyuanvideo_text_33x3600_t256_h24_d128.md",
+    ("k_attn_bf16", 4, "explicit"): "k_attn_bf16_sparse_vdit_21x1560_h40_d128.md",
+    ("k_attn_fp8", 2, "virtual"): "k_attn_fp8_hunyuanvideo_33x3600_h24_d128.md",
+    ("k_attn_fp8pv", 2, "virtual"): "k_attn_fp8pv_hunyuanvideo_33x3600_h24_d128.md",
+}
 
 
-def attn_source_sha256():
+def source_sha256(kernel):
+    """sha256 over the sources of a timed kernel (k_attn_fp8pv is built from
+    the k_attn_fp8 file)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SOURCES["k_attn_fp8" if kernel == "k_attn_fp8pv" else kernel]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per attention dispatch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel
-    source has changed since the counters were taken."""
-    import hashlib
-    try:
-        text = open(PROFILE_SUMMARY).read()
-        sha = attn_source_sha256()
-    except OSError:
-        return None
+def read_record(path):
+    """The '- key: value' lines of a summary's record block."""
     rec = {}
-    for line in text.splitlines():
-        if line.startswith("- attn_"):
+    for line in open(path).read().splitlines():
+        if line.startswith("- record_"):
             k, _, v = line[2:].partition(":")
             rec[k.strip()] = v.strip()
-    if rec.get("attn_kernel_source_sha256") != sha or "attn_traffic_bytes_per_dispatch" not in rec:
+    return rec
+
+
+def recorded_traffic(kernel, config, layout):
+    """HBM bytes per dispatch of the timed kernel from the committed rocprofv3
+    counter summary of this workload and layout (FETCH_SIZE + WRITE_SIZE,
+    calibrated), or None when there is none or the kernel's sources have
+    changed since the counters were taken."""
+    name = TRAFFIC_RECORDS.get((kernel, config, layout))
+    if name is None:
         return None
-    return float(rec["attn_traffic_bytes_per_dispatch"])
+    try:
+        rec = read_record(os.path.join(ROOT, "profiles", name))
+        sha = source_sha256(kernel)
+    except OSError:
+        return None
+    if rec.get("record_source_sha256") != sha or rec.get("record_kernel") != kernel or \
+            "record_traffic_bytes_per_dispatch" not in rec:
+        return None
+    return float(rec["record_traffic_bytes_per_dispatch"])
 
 
 def log(msg):
@@ -353,67 +379,81 @@ def main():
         if args.fp8_pv:
             v8 = torch.empty(H * nkt * d * 64, dtype=torch.uint8, device=dev)
             svh = torch.empty(H, dtype=torch.float32, device=dev)
-    flags = svg.VIRTUAL_PERMUTE if args.virtual else 0
-    if not args.virtual:
-        qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
-    else:
-        qp = kp = vp = op = None
     modes_fixed = None if profile else torch.from_numpy(inp["kinds"].astype(np.int32)).to(dev)
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(marks):
-        """One layer; records an event after each stage into marks (list)."""
-        marks.append(ev()); marks[-1].record(stream)
-        if profile:
-            svg.svg_profile_heads(geom, q, k, v, rows, labels, stats, ws)
-            modes = labels
+    def timed_layer(virtual):
+        """Warmup, then args.steps timed layers with temporal heads through
+        explicit permuted copies (virtual False) or the index map (True).
+        Returns (ms per step, per-stage ms means [profile, blocks, permute or
+        quantise, attention, inverse permute], wall ms per step)."""
+        flags = svg.VIRTUAL_PERMUTE if virtual else 0
+        if not virtual:
+            qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
         else:
-            modes = modes_fixed
-        marks.append(ev()); marks[-1].record(stream)
-        svg.svg_build_blocks(geom, modes, BM, BN, ranges, order)
-        marks.append(ev()); marks[-1].record(stream)
-        if args.fp8:
-            svg.svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk)
-            if args.fp8_pv:
-                svg.svg_quantize_v(geom, v, modes, v8, svh)
-        elif not args.virtual:
-            for s_, d_ in ((q, qp), (k, kp), (v, vp)):
-                svg.svg_layout_permute(geom, s_, d_, modes=modes)
-        marks.append(ev()); marks[-1].record(stream)
-        if args.fp8_pv:
-            svg.svg_sparse_attention_fp8_pv(geom, q8, sq, k8, sk, v8, svh, o, modes, ranges, order)
-        elif args.fp8:
-            svg.svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, order)
-        else:
-            svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op,
-                                     flags=flags)
-        marks.append(ev()); marks[-1].record(stream)
-        if not args.virtual:
-            svg.svg_layout_permute(geom, op, o, modes=modes, inverse=True)
-        marks.append(ev()); marks[-1].record(stream)
+            qp = kp = vp = op = None
 
-    for i in range(args.warmup):
-        step([])
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-    all_marks = []
-    start, end = ev(), ev()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        m = []
-        step(m)
-        all_marks.append(m)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / args.steps
-    stage = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(5)] for m in all_marks])
-    prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage.mean(axis=0)
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
+        def step(marks):
+            """One layer; records an event after each stage into marks (list)."""
+            marks.append(ev()); marks[-1].record(stream)
+            if profile:
+                svg.svg_profile_heads(geom, q, k, v, rows, labels, stats, ws)
+                modes = labels
+            else:
+                modes = modes_fixed
+            marks.append(ev()); marks[-1].record(stream)
+            svg.svg_build_blocks(geom, modes, BM, BN, ranges, order)
+            marks.append(ev()); marks[-1].record(stream)
+            if args.fp8:
+                svg.svg_quantize_qk(geom, q, k, modes, q8, sq, k8, sk)
+                if args.fp8_pv:
+                    svg.svg_quantize_v(geom, v, modes, v8, svh)
+            elif not virtual:
+                for s_, d_ in ((q, qp), (k, kp), (v, vp)):
+                    svg.svg_layout_permute(geom, s_, d_, modes=modes)
+            marks.append(ev()); marks[-1].record(stream)
+            if args.fp8_pv:
+                svg.svg_sparse_attention_fp8_pv(geom, q8, sq, k8, sk, v8, svh, o, modes, ranges, order)
+            elif args.fp8:
+                svg.svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, order)
+            else:
+                svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op,
+                                         flags=flags)
+            marks.append(ev()); marks[-1].record(stream)
+            if not virtual:
+                svg.svg_layout_permute(geom, op, o, modes=modes, inverse=True)
+            marks.append(ev()); marks[-1].record(stream)
+
+        for i in range(args.warmup):
+            step([])
+        torch.cuda.synchronize()
+        log(f"warmup done ({args.warmup} steps, {'virtual' if virtual else 'explicit'} layout)")
+        all_marks = []
+        start, end = ev(), ev()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            m = []
+            step(m)
+            all_marks.append(m)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = start.elapsed_time(end) / args.steps
+        stage = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(5)] for m in all_marks]).mean(axis=0)
+        log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
+        return ms, stage, wall * 1e3 / args.steps
+
+    ms_per_step, stage, _ = timed_layer(args.virtual)
+    prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage
+    # the other layout of the same layer (bit-identical outputs), reported beside it
+    alt = None
+    if not args.fp8:
+        alt_ms, alt_stage, _ = timed_layer(not args.virtual)
+        alt = (not args.virtual, alt_ms, alt_stage)
 
     # a4 on its own: every head of Q through the layout transformation (one
     # [B, H, L, d] tensor read and written), timed apart from the step
@@ -450,6 +490,7 @@ def main():
     explicit = not args.virtual and n_temporal
     fwd_gbs = 3 * perm_bytes / (perm_ms * 1e-3) / 1e9 if explicit and perm_ms > 0 else None
     inv_gbs = perm_bytes / (inv_ms * 1e-3) / 1e9 if explicit and inv_ms > 0 else None
+    timed_kernel = "k_attn_fp8pv" if args.fp8_pv else "k_attn_fp8" if args.fp8 else "k_attn_bf16"
     result = {
         "metric": "sparse-attn ms/layer + effective TFLOP/s vs bf16 MFMA peak (33x3600x24h x d128)",
         "value": round(step_tflops, 2),
@@ -484,9 +525,16 @@ def main():
         "permute_all_heads_gbs": round(perm_all_gbs, 1),
         "permute_all_heads_frac_of_hbm": round(perm_all_gbs / 8000.0, 4),
         "effective_flops_per_layer": flops,
+        "other_layout": None if alt is None else {
+            "layout": "virtual" if alt[0] else "explicit",
+            "value": round(flops / (alt[1] * 1e-3) / 1e12, 2), "ms_per_step": round(alt[1], 4),
+            "attn_ms": round(float(alt[2][3]), 4), "attn_frac_of_peak": round(flops / (alt[2][3] * 1e-3) / 1e12 / peak, 4),
+            "profile_ms": round(float(alt[2][0]), 4),
+            "permute_fwd_ms": round(float(alt[2][2]), 4), "permute_inv_ms": round(float(alt[2][4]), 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
-                     "traffic": recorded_traffic() if args.config == 2 and not args.virtual and not args.fp8 else None,
+                     "traffic": recorded_traffic(timed_kernel, args.config,
+                                                 "virtual" if args.virtual else "explicit") if bf16 else None,
                      "kernel": ("k_attn_fp8<PV8> (svg_sparse_attention_fp8_pv)" if args.fp8_pv else
                                 "k_attn_fp8 (svg_sparse_attention_fp8)" if args.fp8 else
                                 "k_attn_bf16 (svg_sparse_attention)") if bf16 else "k_attn_f32"},
@@ -494,7 +542,6 @@ def main():
     if args.search and bf16:
         result.update(time_search(args, svg, S, geom, q, k, v, inp, dev, np, torch))
     if args.svg2 and bf16:
-        del qp, kp, vp, op
         result.update(time_svg2(args, svg, S, cfg, dev, np, torch))
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")

@@ -30,8 +30,14 @@
  *  - Return value: SVG_OK, or an error status.  On any error nothing has been
  *    enqueued and no output was touched (except SVG_E_HIP, which reports a
  *    failed launch); svg_last_error() then returns a message (thread-local).
- *  - Device-side contents (modes, rows) are trusted: out-of-range values are
- *    undefined behaviour; the Python binding can check them in debug mode.
+ *  - Device-side contents are read on the device only; the library checks
+ *    none of them.  Modes must be values of svg_mode: any other value is
+ *    undefined behaviour.  A list of sampled rows must hold ascending
+ *    distinct video rows in [T, L); every kernel clamps a row into [T, L) as
+ *    it reads it, so a list that breaks this contract gives unspecified
+ *    labels and statistics but never an access outside the caller's
+ *    buffers.  The Python binding checks both on the host only in debug mode
+ *    (SVG_DEBUG=1 in the environment).
  */
 #ifndef SVG_H
 #define SVG_H
@@ -108,6 +114,19 @@ const char* svg_last_error(void);
  * Errors: SVG_E_INVALID (null outputs), SVG_E_UNSUPPORTED (dtype/d). */
 svg_status svg_tile_config(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN);
 
+/* Row sampling for online profiling (rebuttal: answer on profiling, the
+ * head type decided at every diffusion step and layer from a few query
+ * rows).  Writes `count` distinct video rows of the geometry, drawn
+ * uniformly without replacement from [T, T + N*F) and sorted ascending, to
+ * the HOST array rows[count] (the caller copies it to the device for
+ * svg_profile_heads / svg_layer_forward).  The draw is a pure function of
+ * (N*F, T, count, seed): Floyd's sampling (Bentley and Floyd, CACM 1987) on
+ * SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) started at `seed`; pass a
+ * new seed per call for fresh rows.  Host only: no device work, no stream.
+ * Errors: SVG_E_INVALID (geometry, count outside [0, N*F], rows NULL with
+ * count > 0), SVG_E_UNSUPPORTED (geometry). */
+svg_status svg_sample_rows(const svg_geom* geom, int32_t count, uint64_t seed, int32_t* rows);
+
 /* Workspace needed by svg_layer_forward for this geometry, input dtype,
  * number of sampled rows (0 = no profiling) and flags.  Also covers
  * svg_profile_heads (which needs a subset).  With SVG_FLAG_MODE_SEARCH: the
@@ -119,7 +138,8 @@ svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_
 /* Online profiling (rebuttal: answer on when profiling happens; abstract:
  * head types predicted online).  For every (b, h), on the n_rows sampled
  * query rows `rows` (device int32, ascending distinct video rows in [T, L),
- * shared by all heads), computes full, spatial and temporal attention,
+ * shared by all heads, e.g. from svg_sample_rows; trusted, see the
+ * conventions above), computes full, spatial and temporal attention,
  *   rel_m = sum (O_m - O_full)^2 / sum O_full^2   over rows x d,
  * and writes labels[b*H+h] = SPATIAL if rel_s <= rel_t else TEMPORAL, or FULL
  * when min(rel_s, rel_t) >= fallback_rel_mse; stats[(b*H+h)*3 + {0,1,2}] =

@@ -17,6 +17,7 @@ import os
 __all__ = [
     "SPATIAL", "TEMPORAL", "FULL", "SKIP", "WINDOW", "STRIPE", "F32", "BF16", "VIRTUAL_PERMUTE", "MODE_SEARCH",
     "FP8_SCORES", "SEARCH_CANDIDATES", "Geom", "SvgError", "svg_abi_version", "svg_last_error", "svg_tile_config",
+    "svg_sample_rows",
     "svg_workspace_bytes", "svg_profile_heads", "svg_search_modes", "svg_build_blocks", "svg_layout_permute",
     "svg_sparse_attention", "svg_quantize_qk", "svg_sparse_attention_fp8", "svg_quantize_v",
     "svg_sparse_attention_fp8_pv", "FP8_PV", "svg_layer_forward", "svg_layer_forward_noalloc",
@@ -147,6 +148,7 @@ def _lib():
             "svg_abi_version": ([], i32),
             "svg_last_error": ([], ctypes.c_char_p),
             "svg_tile_config": ([i32, i32, P(i32), P(i32)], i32),
+            "svg_sample_rows": ([g, i32, ctypes.c_uint64, P(i32)], i32),
             "svg_workspace_bytes": ([g, i32, i32, i32, P(ctypes.c_size_t)], i32),
             "svg_profile_heads": ([g, i32, vp, vp, vp, S, vp, i32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp],
                                   i32),
@@ -304,6 +306,19 @@ def svg_tile_config(dtype, d):
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     _check(_lib().svg_tile_config(dtype, d, ctypes.byref(bm), ctypes.byref(bn)))
     return bm.value, bn.value
+
+
+def svg_sample_rows(geom, count, seed):
+    """`count` distinct video rows of `geom` ([T, T + N*F)), uniform without
+    replacement and ascending, as a host int32 numpy array (a pure function of
+    the geometry, count and seed; the library draws them, see svg.h)."""
+    import numpy as np
+
+    rows = np.empty(max(int(count), 0), dtype=np.int32)
+    g = geom.c()
+    _check(_lib().svg_sample_rows(ctypes.byref(g), int(count), int(seed) & (2**64 - 1),
+                                  rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return rows
 
 
 def svg_workspace_bytes(geom, dtype, n_rows=0, flags=0):

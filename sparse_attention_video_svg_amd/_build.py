@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsvg.so")
 
-SOURCES = ["api.cpp", "blocks.hip", "permute.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip", "svg2.hip", "profile.hip", "static_ws.hip"]
+SOURCES = ["api.cpp", "blocks.hip", "permute.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip", "svg2.hip", "profile.hip", "static_ws.hip", "sample.cpp"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of every kernel (see the design notes).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -529,6 +529,18 @@ svg_status svg_tile_config(svg_dtype dtype, int32_t d, int32_t* BM, int32_t* BN)
   return tile_config_impl(dtype, d, BM, BN);
 }
 
+svg_status svg_sample_rows(const svg_geom* geom, int32_t count, uint64_t seed, int32_t* rows) {
+  KGeom g;
+  TRY(check_geom(geom, &g));
+  const int64_t n = (int64_t)g.N * g.F;
+  if (count < 0 || count > n) return fail(SVG_E_INVALID, "count=%d must be in [0, N*F = %lld]", count, (long long)n);
+  if (count == 0) return SVG_OK;
+  if (!rows) return fail(SVG_E_INVALID, "rows is NULL");
+  sample_sorted(n, count, seed, rows);
+  for (int32_t r = 0; r < count; ++r) rows[r] += g.T;
+  return SVG_OK;
+}
+
 svg_status svg_workspace_bytes(const svg_geom* geom, svg_dtype dtype, int32_t n_rows, int32_t flags,
                                size_t* bytes) {
   KGeom g;

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
 
   const int rk = chunk * BMW + wave * 32 + (lane & 31);
   const bool valid = rk < n_rows;
-  const int x = rows[valid ? rk : n_rows - 1];
+  const int x = sampled_row(g, rows[valid ? rk : n_rows - 1]);
   int lo, hi;
   if (VIRT) {  // the row's band in token-major order: x = T + i*F + j -> T + j*N + i
     const int u = x - g.T;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
   run_sweep<D, VIRT, WAVES, STAGES>(st, qf, k + base, v + base, s.x, g, rg, lo, hi, valid, lds, wave, lane);
   if (valid) {
     // temporal rows come in position order; ord_r maps them back
-    const int r = VIRT ? ord_r[rk] : rk;
+    const int r = VIRT ? min(max(ord_r[rk], 0), n_rows - 1) : rk;  // (a permutation for valid rows)
     const int64_t o = (((int64_t)bh * n_rows + r) * nsplit + split) * nstates + state;
     store_partial<D>(st, part_acc + o * D, part_ml + o * 2, hh);
   }

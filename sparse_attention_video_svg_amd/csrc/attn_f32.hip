@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) void k_profile_f32(KGeom g, const float* __rest
   const int bh = blockIdx.y, r = blockIdx.x;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-  const int x = rows[r];
+  const int x = sampled_row(g, rows[r]);
   for (int c = lane; c < D; c += 64) qs[c] = q[base + (int64_t)x * s.x + c];
   __syncthreads();
   // spatial run of frames and temporal band of positions of this row

@@ -21,7 +21,9 @@ namespace svg {
 
 // Position order of the sampled rows (ascending, distinct video rows): the
 // key of row x = T + i*F + j is its token-major index j*N + i, and its rank
-// is the number of rows with a smaller key (keys are distinct).
+// is the number of rows with a smaller key (keys are distinct).  Rows are
+// clamped into [T, L) as read, and ranks stay in [0, n_rows) whatever the
+// list holds, so a list that breaks the contract is never a memory error.
 // k_prof_rank_lds: all keys staged in LDS, each thread counts over them.
 // k_prof_rank (more rows than fit): per frame, a binary search for the
 // rows at smaller positions, plus the row at the same position if its
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void k_prof_rank_lds(KGeom g, const int32_t* _
   for (int r = threadIdx.x; r < n4; r += blockDim.x) {
     int key = INT_MAX;
     if (r < n_rows) {
-      const int u = rows[r] - g.T;
+      const int u = sampled_row(g, rows[r]) - g.T;
       const int i = fastdiv(u, g.divF_mul, g.divF_shift);
       key = (u - i * g.F) * g.N + i;
     }
@@ -58,11 +60,14 @@ __global__ __launch_bounds__(256) void k_prof_rank_lds(KGeom g, const int32_t* _
   if (r >= n_rows) return;
   const int own = keys[r];
   int rank = 0;
+  // equal keys (a repeated row) are ranked by their index, so the ranks are
+  // a permutation of [0, n_rows) for any list
   for (int o = 0; o < n4; o += 4) {
     const int4 k4 = *reinterpret_cast<const int4*>(keys + o);
-    rank += (k4.x < own) + (k4.y < own) + (k4.z < own) + (k4.w < own);
+    rank += (k4.x < own || (k4.x == own && o < r)) + (k4.y < own || (k4.y == own && o + 1 < r)) +
+            (k4.z < own || (k4.z == own && o + 2 < r)) + (k4.w < own || (k4.w == own && o + 3 < r));
   }
-  ord_x[rank] = rows[r];
+  ord_x[rank] = sampled_row(g, rows[r]);
   ord_r[rank] = r;
 }
 
@@ -70,7 +75,7 @@ __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n
                             int32_t* __restrict__ ord_r) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n_rows) return;
-  const int x = rows[r];
+  const int x = sampled_row(g, rows[r]);
   const int u = x - g.T;
   const int i = fastdiv(u, g.divF_mul, g.divF_shift), j = u - i * g.F;
   int rank = 0;
@@ -81,6 +86,7 @@ __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n
     rank += c - a;
     if (f < i && c < n_rows && rows[c] == fb + j) ++rank;
   }
+  rank = min(max(rank, 0), n_rows - 1);  // (exact for a valid list)
   ord_x[rank] = x;
   ord_r[rank] = r;
 }

@@ -16,6 +16,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define SVG_LDS __attribute__((address_space(3)))
 
+// A sampled query row as read from a caller's row list, clamped into the
+// video rows [T, L): the list is trusted to hold ascending distinct video
+// rows, and the clamp keeps any other contents from addressing outside the
+// tensors (they give unspecified labels instead).
+__device__ __forceinline__ int sampled_row(const KGeom& g, int x) { return min(max(x, g.T), g.L - 1); }
+
 // Active keys of query row x in the head's working layout are
 // [0, T) U [lo, hi) (text keys, then one contiguous run of video keys).
 // Closed forms (u = x - T, video index; rebuttal answer to Weakness 1):

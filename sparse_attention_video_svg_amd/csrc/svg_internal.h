@@ -30,6 +30,10 @@ struct DevTopo {
 };
 hipError_t device_topology(DevTopo* t);
 
+// count distinct integers of [0, n), uniform without replacement, ascending
+// (host; sample.cpp)
+void sample_sorted(int64_t n, int32_t count, uint64_t seed, int32_t* out);
+
 // Division of a non-negative int32 by an invariant positive divisor with one
 // multiply-high, after Granlund and Montgomery, "Division by invariant
 // integers using multiplication" (PLDI 1994): with s = ceil(log2 dv) and

@@ -1,5 +1,7 @@
 """CPU checks of bench.py's bookkeeping: the closed-form pair counts that
 turn kernel time into effective TFLOP/s equal the oracle's mask sums."""
+import os
+
 import numpy as np
 import pytest
 
@@ -47,3 +49,36 @@ def test_search_key_count_matches_oracle_intervals(oracle_lib, N, F, T):
             for mode in (oracle.FULL, oracle.WINDOW, oracle.TEMPORAL, oracle.STRIPE):
                 want += sum(h - l for l, h in oracle.row_intervals(g, mode, int(x)))
         assert bench.search_keys(geom, rows) == want
+
+
+def test_traffic_record_is_guarded_by_source_hash(tmp_path, monkeypatch):
+    """A committed counter record feeds roofline.traffic only while the hash of
+    its kernel's sources is the one it was taken at, and only for its own
+    kernel, workload and layout."""
+    (tmp_path / "profiles").mkdir()
+    name = bench.TRAFFIC_RECORDS[("k_attn_bf16", 2, "explicit")]
+    sha = bench.source_sha256("k_attn_bf16")
+
+    def write(kernel, digest):
+        (tmp_path / "profiles" / name).write_text(
+            f"# summary\n\n- record_kernel: {kernel}\n- record_source_sha256: {digest}\n"
+            "- record_traffic_bytes_per_dispatch: 7.5e+09\n")
+
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    write("k_attn_bf16", sha)
+    assert bench.recorded_traffic("k_attn_bf16", 2, "explicit") == 7.5e9
+    assert bench.recorded_traffic("k_attn_bf16", 2, "virtual") is None
+    assert bench.recorded_traffic("k_attn_bf16", 0, "explicit") is None
+    write("k_attn_bf16", "0" * 64)
+    assert bench.recorded_traffic("k_attn_bf16", 2, "explicit") is None
+    write("k_attn_fp8", sha)
+    assert bench.recorded_traffic("k_attn_bf16", 2, "explicit") is None
+
+
+def test_kernel_source_sets_exist_and_differ():
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        for f in files:
+            assert os.path.isfile(os.path.join(bench.CSRC, f)), (kernel, f)
+    shas = {k: bench.source_sha256(k) for k in bench.KERNEL_SOURCES}
+    assert len(set(shas.values())) == len(shas)
+    assert bench.source_sha256("k_attn_fp8pv") == shas["k_attn_fp8"]

@@ -93,3 +93,29 @@ def test_profile_every_video_row(case):
         rs, rt = ref[0], ref[1]
         if abs(rs - rt) > 0.05 * max(rs, rt) + 1e-3 and abs(min(rs, rt) - 0.05) > 5e-3:
             assert lab[h] == want, (h, lab[h], want, st[h], ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_profile_rows_outside_contract(d, monkeypatch):
+    """A row list that breaks the contract (rows outside [T, L), repeats, no
+    order) is clamped into [T, L) as read: profiling then equals the oracle's
+    on the clamped list, row for row, and nothing is read outside q, k, v."""
+    monkeypatch.setattr(svg, "DEBUG", False)
+    N, F, T, H = 4, 64, 3, 2
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=1, a2=8)
+    inp = S.small_config(N, F, T, H, d, 1, 8, [S.SPATIAL, S.TEMPORAL], seed=77 + d)
+    q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
+    rows_np = np.array([g.L + 40, -7, T + 10, T + 10, g.L - 1, T + 130, 0, T + 5, T + 130, 2**31 - 1],
+                       dtype=np.int32)
+    clamped = np.clip(rows_np.astype(np.int64), T, g.L - 1)
+    print(f"\n[profile rows outside the contract d={d} L={g.L}]", flush=True)
+    labels = torch.empty(H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(H * 3, dtype=torch.float32, device="cuda")
+    ws = svg.alloc_workspace(g, svg.BF16, rows_np.size, svg.VIRTUAL_PERMUTE)
+    svg.svg_profile_heads(g, q, k, v, torch.from_numpy(rows_np).cuda(), labels, stats, ws)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy().reshape(H, 3)
+    og = ogeom(g)
+    for h in range(H):
+        _, ref = oracle.profile_head(og, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), clamped)
+        np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
