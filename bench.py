@@ -76,6 +76,8 @@ KERNEL_SOURCES = {
     "k_attn_fp8": ("attn_fp8.hip", "attn_common.h", "svg_device.h", "svg_internal.h", "svg_sched.h"),
     "k_svg2_attn": ("svg2.hip", "attn_common.h", "svg_device.h", "svg_internal.h", "svg_sched.h"),
     "k_permute": ("permute.hip", "svg_device.h", "svg_internal.h"),
+    "k_prof_sweep": ("attn_bf16.hip", "attn_common.h", "profile.hip", "svg_device.h", "svg_internal.h",
+                     "svg_sched.h"),
 }
 # rocprofv3 summaries under profiles/ holding an HBM-traffic record, by
 # (timed kernel, workload, layout)
@@ -319,6 +321,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--virtual", action="store_true",
                     help="temporal heads gather through the index map instead of explicit permutes")
+    ap.add_argument("--one-layout", action="store_true",
+                    help="time only the headline layout (profiler runs: both layouts launch the same kernels)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--search", action="store_true", help="also time svg_search_modes on the same inputs")
     ap.add_argument("--fp8", action="store_true",
@@ -451,7 +455,7 @@ def main():
     prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage
     # the other layout of the same layer (bit-identical outputs), reported beside it
     alt = None
-    if not args.fp8:
+    if not args.fp8 and not args.one_layout:
         alt_ms, alt_stage, _ = timed_layer(not args.virtual)
         alt = (not args.virtual, alt_ms, alt_stage)
 

@@ -175,29 +175,21 @@ __device__ __forceinline__ void store_partial(const Flash<D>& st, float* acc, fl
 // chunks of rows sharing one slice of one head run together on one XCD and
 // share those K/V tiles in its L2.  The partial state of (row, slice) goes to
 // slot ((bh * n_rows + row) * nsplit + slice) * nstates + state.
+// One work item of a sweep: rows [chunk * BMW, +BMW) of the sampled rows in
+// `rows` order, key slice `split` of their union, head bh, under `mode`.
 template <int D, bool VIRT, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep(
-    KGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    svg_strides s, const int32_t* __restrict__ rows, const int32_t* __restrict__ ord_r, int32_t n_rows,
-    int32_t nsplit, int32_t total, int32_t mode, int32_t state, int32_t nstates, float* __restrict__ part_acc,
-    float* __restrict__ part_ml) {
-  using C = TileCfg<D, WAVES>;
+__device__ __forceinline__ void prof_item(const KGeom& g, const __bf16* __restrict__ q,
+                                          const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                          const svg_strides& s, const int32_t* __restrict__ rows,
+                                          const int32_t* __restrict__ ord_r, int32_t n_rows, int32_t nsplit,
+                                          int chunk, int split, int bh, int32_t mode, int32_t state, int32_t nstates,
+                                          float* __restrict__ part_acc, float* __restrict__ part_ml,
+                                          __bf16 (*lds)[2][TileCfg<D, WAVES>::TILE_ELEMS], int (*wb)[WAVES],
+                                          int wave, int lane) {
   constexpr int BMW = 32 * WAVES;
-  extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
-  auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
-  __shared__ int wb[2][WAVES];
-  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  const int w = blockIdx.x;
-  const int logical = xcd_logical(w, g.nxcd, kXcdRun);
-  if (logical >= total) return;
-  const int chunks = (n_rows + BMW - 1) / BMW;
-  const int chunk = logical % chunks;
-  const int split = (logical / chunks) % nsplit, bh = logical / chunks / nsplit;
+  const int hh = lane >> 5;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t base = (int64_t)b * s.b + (int64_t)h * s.h;
-
   const int rk = chunk * BMW + wave * 32 + (lane & 31);
   const bool valid = rk < n_rows;
   const int x = sampled_row(g, rows[valid ? rk : n_rows - 1]);
@@ -251,6 +243,62 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep
   }
 }
 
+template <int D, bool VIRT, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, (WAVES <= 6 ? 2 : 1)) void k_prof_sweep(
+    KGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    svg_strides s, const int32_t* __restrict__ rows, const int32_t* __restrict__ ord_r, int32_t n_rows,
+    int32_t nsplit, int32_t total, int32_t mode, int32_t state, int32_t nstates, float* __restrict__ part_acc,
+    float* __restrict__ part_ml) {
+  using C = TileCfg<D, WAVES>;
+  constexpr int BMW = 32 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
+  auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
+  __shared__ int wb[2][WAVES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, g.nxcd, kXcdRun);
+  if (logical >= total) return;
+  const int chunks = (n_rows + BMW - 1) / BMW;
+  const int chunk = logical % chunks;
+  const int split = (logical / chunks) % nsplit, bh = logical / chunks / nsplit;
+  prof_item<D, VIRT, WAVES, STAGES>(g, q, k, v, s, rows, ord_r, n_rows, nsplit, chunk, split, bh, mode, state,
+                                    nstates, part_acc, part_ml, lds, wb, wave, lane);
+}
+
+// All masks of a call in one launch, their work items dealt round-robin
+// (item i of mask m at position i * nmask + m): the full-attention items keep
+// the matrix cores busy while the short-run masks wait on their loads, and
+// the two kinds share each CU instead of running one after the other.  State
+// m is mask m; the temporal band goes through the index map (rows in position
+// order ord_x, ord_r).
+template <int D, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, 2) void k_prof_multi(
+    KGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    svg_strides s, const int32_t* __restrict__ rows, const int32_t* __restrict__ ord_x,
+    const int32_t* __restrict__ ord_r, int32_t n_rows, int32_t nsplit, int32_t items, int4 masks, int32_t nmask,
+    float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  using C = TileCfg<D, WAVES>;
+  constexpr int BMW = 32 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) __bf16 lds_raw[];
+  auto lds = reinterpret_cast<__bf16 (*)[2][C::TILE_ELEMS]>(lds_raw);  // [stage][K, V]
+  __shared__ int wb[2][WAVES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, g.nxcd, kXcdRun);
+  if (logical >= items * nmask) return;
+  const int m = logical % nmask, item = logical / nmask;
+  const int mode = m == 0 ? masks.x : m == 1 ? masks.y : m == 2 ? masks.z : masks.w;
+  const int chunks = (n_rows + BMW - 1) / BMW;
+  const int chunk = item % chunks;
+  const int split = (item / chunks) % nsplit, bh = item / chunks / nsplit;
+  if (mode == SVG_TEMPORAL)
+    prof_item<D, true, WAVES, STAGES>(g, q, k, v, s, ord_x, ord_r, n_rows, nsplit, chunk, split, bh, mode, m, nmask,
+                                      part_acc, part_ml, lds, wb, wave, lane);
+  else
+    prof_item<D, false, WAVES, STAGES>(g, q, k, v, s, rows, nullptr, n_rows, nsplit, chunk, split, bh, mode, m,
+                                       nmask, part_acc, part_ml, lds, wb, wave, lane);
+}
+
 template <int D, bool OUT_BF16>
 static hipError_t launch_attn(const KGeom& g, const AttnPtrs& a, int32_t nQT, int64_t grid, int64_t total,
                               hipStream_t st) {
@@ -295,11 +343,40 @@ static hipError_t launch_prof(const KGeom& g, const __bf16* q, const __bf16* k, 
 // measured faster than 2 and 8 on the HunyuanVideo-shaped layer)
 constexpr int kProfWavesBand = 4;
 
+// waves per workgroup of the one-launch sweep of all masks; used at d 64,
+// where it measured 17 % faster than one launch per mask on the
+// CogVideoX-like layer (at d 128, 2 % slower on the HunyuanVideo-shaped one)
+constexpr int kProfWavesMulti = 4;
+
+template <int D>
+static hipError_t launch_multi(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
+                               const int32_t* rows, const int32_t* ord_x, const int32_t* ord_r, int32_t n_rows,
+                               int32_t nsplit, const int32_t* modes, int32_t nstates, float* acc, float* ml,
+                               hipStream_t st) {
+  constexpr int W = kProfWavesMulti, S = kAttnStages;
+  if (nstates < 1 || nstates > 4) return hipErrorInvalidValue;
+  const size_t lds = (size_t)S * 2 * TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
+  auto kern = k_prof_multi<D, W, S>;
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
+  const int64_t chunks = (n_rows + 32 * W - 1) / (32 * W);
+  const int64_t items = chunks * nsplit * g.B * g.H;
+  const int64_t grid = xcd_grid(items * nstates, g.nxcd, kXcdRun);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const int4 masks = make_int4(modes[0], nstates > 1 ? modes[1] : 0, nstates > 2 ? modes[2] : 0,
+                               nstates > 3 ? modes[3] : 0);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, st, g, q, k, v, s, rows, ord_x, ord_r, n_rows,
+                     nsplit, (int32_t)items, masks, nstates, acc, ml);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_sweeps(const KGeom& g, const __bf16* q, const __bf16* k, const __bf16* v, svg_strides s,
                                 const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
                                 const int32_t* ord_r, const int32_t* modes, int32_t nstates, float* acc, float* ml,
                                 hipStream_t st) {
+  if constexpr (D == 64)
+    return launch_multi<D>(g, q, k, v, s, rows, ord_x, ord_r, n_rows, ksplit, modes, nstates, acc, ml, st);
   for (int32_t i = 0; i < nstates; ++i) {
     hipError_t e;
     // masks with short runs per row take workgroups of kProfWavesBand waves (fewer rows, so the union of
