@@ -84,6 +84,7 @@ KERNEL_SOURCES = {
 TRAFFIC_RECORDS = {
     ("k_attn_bf16", 1, "explicit"): "k_attn_bf16_cogvideox_13x4080_h48_d64.md",
     ("k_attn_bf16", 2, "explicit"): "k_attn_bf16_hunyuanvideo_33x3600_h24_d128.md",
+    ("k_attn_bf16", 2, "virtual"): "k_attn_bf16_virtual_hunyuanvideo_33x3600_h24_d128.md",
     ("k_attn_bf16", 3, "explicit"): "k_attn_bf16_hunyuanvideo_text_33x3600_t256_h24_d128.md",
     ("k_attn_bf16", 4, "explicit"): "k_attn_bf16_sparse_vdit_21x1560_h40_d128.md",
     ("k_attn_fp8", 2, "virtual"): "k_attn_fp8_hunyuanvideo_33x3600_h24_d128.md",
