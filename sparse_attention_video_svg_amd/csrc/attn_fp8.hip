@@ -321,6 +321,29 @@ __device__ __forceinline__ void score_tile_fp8(const uint8_t* lk, const i32x8* q
   }
 }
 
+// As score_tile_fp8 with the query fragments read from LDS (the lane's 16-byte
+// halves at lq + (2 * ks + half) * 1024 + 16 * lane, written by the lane
+// itself before the sweep).  The FP8 P.V kernel keeps them there at d 128,
+// where at its 168-register cap it otherwise spills one of them, and the
+// reload from scratch, counted with the vector-memory loads, made every
+// tile's first score MFMA wait for the next tile's K/V loads as well
+// (-5 % attention time; at d 64, where nothing spills, +1 %).
+template <int D>
+inline constexpr bool kFp8PvQInLds = D == 128;
+template <int D>
+__device__ __forceinline__ void score_tile_fp8_lq(const uint8_t* lk, const uint8_t* lq, int lane, f32x16& s0,
+                                                  f32x16& s1) {
+  constexpr int KS = D / 64;
+  i32x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const i32x4 a = *reinterpret_cast<const i32x4*>(lq + (2 * ks) * 1024 + 16 * lane);
+    const i32x4 b = *reinterpret_cast<const i32x4*>(lq + (2 * ks + 1) * 1024 + 16 * lane);
+    qf[ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  score_tile_fp8<D>(lk, qf, lane, s0, s1);
+}
+
 // Lock-step sweep with fp8 scores (as sweep() in attn_common.h): 2-stage
 // ring, one barrier per tile, masks on partial tiles, idle tiles skipped per
 // wave.  sl2q = scale * log2(e) * sq(row); sk: this head's K tile scales.
@@ -490,7 +513,8 @@ struct Flash8 {
 
 // Sweep with fp8 scores and fp8 P.V (as sweep_fp8).
 template <int D, int WAVES>
-__device__ __forceinline__ void sweep_fp8pv(Flash8<D>& st, const i32x8* qf, const Fp8PvLoader<D, WAVES>& ld,
+__device__ __forceinline__ void sweep_fp8pv(Flash8<D>& st, const i32x8* qf, const uint8_t* lq,
+                                            const Fp8PvLoader<D, WAVES>& ld,
                                             const KGeom& g, int4 rg, int lo, int hi, bool valid, float sl2q,
                                             const float* __restrict__ sk, uint8_t* lds_k0, uint8_t* lds_v0,
                                             int wave, int lane) {
@@ -518,7 +542,10 @@ __device__ __forceinline__ void sweep_fp8pv(Flash8<D>& st, const i32x8* qf, cons
     if (wave_rows && !idle) {
       const bool full = (kt1 <= T) || (max(kt0, T) >= max_lo && kt1 <= min_hi);
       f32x16 s0, s1;
-      score_tile_fp8<D>(lk, qf, lane, s0, s1);
+      if constexpr (kFp8PvQInLds<D>)
+        score_tile_fp8_lq<D>(lk, lq, lane, s0, s1);
+      else
+        score_tile_fp8<D>(lk, qf, lane, s0, s1);
       if (!full) mask_tile(s0, s1, kt0, hh, T, lo, hi);
       const i32x8 p8 = st.softmax(s0, s1, sl2q * sk[kt]);
       st.pv(p8, lv, lane);
@@ -599,7 +626,7 @@ __device__ __forceinline__ void attn_tile_fp8(const KGeom& g, const Fp8Ptrs& a, 
 // One query tile with FP8 P.V (Q8, O through the index map for TEMPORAL heads).
 template <int D, bool OUT_BF16, bool VIRT, int WAVES>
 __device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a, int bh, int qt, int rq, int mode, int nQT,
-                                                uint8_t* lds_k, uint8_t* lds_v, int wave, int lane) {
+                                                uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_q, int wave, int lane) {
   constexpr int BMW = 32 * WAVES;
   const int hh = lane >> 5;
   const int b = bh / g.H, h = bh % g.H;
@@ -618,26 +645,42 @@ __device__ __forceinline__ void attn_tile_fp8pv(const KGeom& g, const Fp8Ptrs& a
   const int xqc = valid ? xq : g.L - 1;
   const int xs = phys(xqc);
   const uint8_t* qrow = a.q8 + ((int64_t)bh * g.L + xs) * D + 32 * hh;
+  // the query fragments, in registers or (d 128) in this wave's own LDS
+  // region (16-byte halves, lane-contiguous: conflict-free reads)
   i32x8 qf[D / 64];
+  uint8_t* lq = lds_q + wave * (D / 64) * 2048;
 #pragma unroll
-  for (int ks = 0; ks < D / 64; ++ks) qf[ks] = *reinterpret_cast<const i32x8*>(qrow + 64 * ks);
+  for (int ks = 0; ks < D / 64; ++ks) {
+    qf[ks] = *reinterpret_cast<const i32x8*>(qrow + 64 * ks);
+    if constexpr (kFp8PvQInLds<D>) {
+      *reinterpret_cast<i32x4*>(lq + (2 * ks) * 1024 + 16 * lane) = __builtin_shufflevector(qf[ks], qf[ks], 0, 1, 2, 3);
+      *reinterpret_cast<i32x4*>(lq + (2 * ks + 1) * 1024 + 16 * lane) =
+          __builtin_shufflevector(qf[ks], qf[ks], 4, 5, 6, 7);
+    }
+  }
   const float sl2q = g.scale_log2 * a.sq[(int64_t)bh * g.L + xs];
   int lo, hi;
   row_interval(g, mode, xqc, lo, hi);
 
   Flash8<D> st;
-  sweep_fp8pv<D, WAVES>(st, qf, ld, g, rg, lo, hi, valid, sl2q, a.sk + (int64_t)bh * a.nKT, lds_k, lds_v, wave,
-                        lane);
+  sweep_fp8pv<D, WAVES>(st, qf, lq, ld, g, rg, lo, hi, valid, sl2q, a.sk + (int64_t)bh * a.nKT, lds_k, lds_v,
+                        wave, lane);
 
   // every lane holds its row's whole weight sum (the ones-MFMA sums all keys)
   const float inv = st.l > 0.f ? a.svh[bh] / st.l : 0.f;
-  if (valid) {
-    char* orow = static_cast<char*>(a.o) + (obase + (int64_t)phys(xq) * a.so.x) * OE;
+  // the output row and column offset are formed anew from the lane id (read
+  // in asm so that it is not shared with the one taken before the sweep), so
+  // that nothing of them stays live across the key loop
+  int lid;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+  const int xo = qt * BMW + wave * 32 + (lid & 31), ho = lid >> 5;
+  if (xo < g.L) {
+    char* orow = static_cast<char*>(a.o) + (obase + (int64_t)phys(xo) * a.so.x) * OE;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hh;
+        const int d0 = db * 32 + 8 * g4 + 4 * ho;
         f32x4 v4 = {st.o[db][4 * g4] * inv, st.o[db][4 * g4 + 1] * inv, st.o[db][4 * g4 + 2] * inv,
                     st.o[db][4 * g4 + 3] * inv};
         if (OUT_BF16) {
@@ -686,10 +729,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 3 : 1) void k_attn_fp8(KGe
   }
   if constexpr (PV8) {
     uint8_t* lds_v = lds8 + 2 * Fp8Cfg<D>::TILE_BYTES;
+    uint8_t* lds_q = lds_v + 2 * V8Cfg<D>::TILE_BYTES;  // [WAVES][D / 64][2][64 lanes x 16 B]
     if (mode == SVG_TEMPORAL)
-      attn_tile_fp8pv<D, OUT_BF16, true, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8pv<D, OUT_BF16, true, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, lds_q, wave, lane);
     else
-      attn_tile_fp8pv<D, OUT_BF16, false, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, wave, lane);
+      attn_tile_fp8pv<D, OUT_BF16, false, WAVES>(g, a, bh, qt, rq, mode, nQT, lds_k, lds_v, lds_q, wave, lane);
   } else {
     __bf16* lds_v = reinterpret_cast<__bf16*>(lds8 + 2 * Fp8Cfg<D>::TILE_BYTES);
     if (mode == SVG_TEMPORAL)
@@ -746,7 +790,9 @@ static hipError_t launch_fp8(const KGeom& g, const Fp8Ptrs& a, int32_t nQT, int6
                              hipStream_t st) {
   constexpr int W = fp8_waves<PV8>();
   const size_t vtile = PV8 ? (size_t)V8Cfg<D>::TILE_BYTES : (size_t)TileCfg<D>::TILE_ELEMS * sizeof(__bf16);
-  const size_t lds = 2 * (size_t)Fp8Cfg<D>::TILE_BYTES + 2 * vtile;
+  // FP8 P.V: plus each wave's query fragments
+  const size_t lds =
+      2 * (size_t)Fp8Cfg<D>::TILE_BYTES + 2 * vtile + (PV8 && kFp8PvQInLds<D> ? (size_t)W * (D / 64) * 2048 : 0);
   auto kern = k_attn_fp8<D, OUT_BF16, W, PV8>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_dynamic_lds((const void*)kern, lds, lds_set); e != hipSuccess) return e;
