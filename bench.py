@@ -392,13 +392,15 @@ def main():
     def timed_layer(virtual):
         """Warmup, then args.steps timed layers with temporal heads through
         explicit permuted copies (virtual False) or the index map (True).
-        Returns (ms per step, per-stage ms means [profile, blocks, permute or
-        quantise, attention, inverse permute], wall ms per step)."""
+        Returns (ms per step, per-stage ms means [profile, blocks, permute of
+        K and V or quantise, attention, (empty)], wall ms per step)."""
         flags = svg.VIRTUAL_PERMUTE if virtual else 0
+        # explicit layout: token-major copies of K and V (the attention kernel
+        # reads Q and writes O of temporal heads through the index map)
         if not virtual:
-            qp, kp, vp, op = (torch.empty_like(t) for t in (q, k, v, o))
+            kp, vp = (torch.empty_like(t) for t in (k, v))
         else:
-            qp = kp = vp = op = None
+            kp = vp = None
 
         def step(marks):
             """One layer; records an event after each stage into marks (list)."""
@@ -416,7 +418,7 @@ def main():
                 if args.fp8_pv:
                     svg.svg_quantize_v(geom, v, modes, v8, svh)
             elif not virtual:
-                for s_, d_ in ((q, qp), (k, kp), (v, vp)):
+                for s_, d_ in ((k, kp), (v, vp)):
                     svg.svg_layout_permute(geom, s_, d_, modes=modes)
             marks.append(ev()); marks[-1].record(stream)
             if args.fp8_pv:
@@ -424,11 +426,9 @@ def main():
             elif args.fp8:
                 svg.svg_sparse_attention_fp8(geom, q8, sq, k8, sk, v, o, modes, ranges, order)
             else:
-                svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, qp=qp, kp=kp, vp=vp, op=op,
-                                         flags=flags)
+                svg.svg_sparse_attention(geom, q, k, v, o, modes, ranges, order, kp=kp, vp=vp, flags=flags)
             marks.append(ev()); marks[-1].record(stream)
-            if not virtual:
-                svg.svg_layout_permute(geom, op, o, modes=modes, inverse=True)
+            # (no inverse permute: temporal heads' outputs are written in place)
             marks.append(ev()); marks[-1].record(stream)
 
         for i in range(args.warmup):
@@ -453,7 +453,7 @@ def main():
         return ms, stage, wall * 1e3 / args.steps
 
     ms_per_step, stage, _ = timed_layer(args.virtual)
-    prof_ms, blocks_ms, perm_ms, attn_ms, inv_ms = stage
+    prof_ms, blocks_ms, perm_ms, attn_ms, _ = stage
     # the other layout of the same layer (bit-identical outputs), reported beside it
     alt = None
     if not args.fp8 and not args.one_layout:
@@ -493,8 +493,7 @@ def main():
     elt = 2 if bf16 else 4
     perm_bytes = 2.0 * n_temporal * L * d * elt  # read + write per permuted head-tensor
     explicit = not args.virtual and n_temporal
-    fwd_gbs = 3 * perm_bytes / (perm_ms * 1e-3) / 1e9 if explicit and perm_ms > 0 else None
-    inv_gbs = perm_bytes / (inv_ms * 1e-3) / 1e9 if explicit and inv_ms > 0 else None
+    fwd_gbs = 2 * perm_bytes / (perm_ms * 1e-3) / 1e9 if explicit and perm_ms > 0 else None  # K and V
     timed_kernel = "k_attn_fp8pv" if args.fp8_pv else "k_attn_fp8" if args.fp8 else "k_attn_bf16"
     result = {
         "metric": "sparse-attn ms/layer + effective TFLOP/s vs bf16 MFMA peak (33x3600x24h x d128)",
@@ -523,9 +522,7 @@ def main():
         "blocks_ms": round(float(blocks_ms), 4),
         "permute_fwd_ms": None if args.fp8 else round(float(perm_ms), 4),
         "quant_ms": round(float(perm_ms), 4) if args.fp8 else None,
-        "permute_inv_ms": round(float(inv_ms), 4),
         "permute_fwd_gbs": None if fwd_gbs is None else round(fwd_gbs, 1),
-        "permute_inv_gbs": None if inv_gbs is None else round(inv_gbs, 1),
         "permute_all_heads_ms": round(perm_all_ms, 4),
         "permute_all_heads_gbs": round(perm_all_gbs, 1),
         "permute_all_heads_frac_of_hbm": round(perm_all_gbs / 8000.0, 4),
@@ -535,7 +532,7 @@ def main():
             "value": round(flops / (alt[1] * 1e-3) / 1e12, 2), "ms_per_step": round(alt[1], 4),
             "attn_ms": round(float(alt[2][3]), 4), "attn_frac_of_peak": round(flops / (alt[2][3] * 1e-3) / 1e12 / peak, 4),
             "profile_ms": round(float(alt[2][0]), 4),
-            "permute_fwd_ms": round(float(alt[2][2]), 4), "permute_inv_ms": round(float(alt[2][4]), 4)},
+            "permute_fwd_ms": round(float(alt[2][2]), 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
                      "traffic": recorded_traffic(timed_kernel, args.config,

@@ -202,10 +202,14 @@ svg_status svg_layout_permute(const svg_geom* geom, svg_dtype dtype, const void*
  * pattern kernels with heads of one mode fused).  One launch runs every head:
  * O = softmax(Q K^T * scale over the head's active keys) V, fp32 accumulation
  * and softmax, bf16 (or fp32) inputs.  SKIP heads write zeros.  TEMPORAL heads
- * run in token-major order: they read qp/kp/vp and write op (strides sp for
- * the three inputs, sop for op), unless flags has SVG_FLAG_VIRTUAL_PERMUTE,
- * in which case they read q/k/v and write o through the index map (qp, kp,
- * vp, op may then be NULL).  ranges / head_order come from svg_build_blocks
+ * run in token-major order: they read kp/vp (the token-major copies of K and
+ * V from svg_layout_permute, strides sp), and qp and op likewise when those
+ * are given (strides sp for qp, sop for op); with qp NULL their query rows
+ * are read from q, with op NULL their outputs written to o, through the
+ * index map (each row once, so o then needs no inverse permute).  With
+ * SVG_FLAG_VIRTUAL_PERMUTE they read q/k/v and write o through the index map
+ * (qp, kp, vp, op may then all be NULL).  Every combination gives the same
+ * outputs, bit for bit.  ranges / head_order come from svg_build_blocks
  * with the BM, BN of svg_tile_config(in, d), which are passed again here for
  * checking.  Supported (in, out): (F32, F32), (BF16, BF16), (BF16, F32).
  * Errors: SVG_E_INVALID, SVG_E_UNSUPPORTED, SVG_E_HIP. */
@@ -328,9 +332,11 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* params, svg_dty
  *   modes_in == NULL: profile on `rows` (writes labels_out, stats_out), else
  *   use modes_in (Sparse-vDiT's fixed per-head modes; no profiling, rows and
  *   stats_out unused, labels_out receives a copy of modes_in);
- *   build key-tile lists; permute Q, K, V of TEMPORAL heads to token-major
- *   (skipped with SVG_FLAG_VIRTUAL_PERMUTE); sparse attention; inverse-permute
- *   the TEMPORAL heads' output into o.
+ *   build key-tile lists; permute K and V of TEMPORAL heads to token-major
+ *   into the workspace (skipped with SVG_FLAG_VIRTUAL_PERMUTE); sparse
+ *   attention, the TEMPORAL heads' query rows read from q and their outputs
+ *   written to o through the index map (svg_sparse_attention with qp and op
+ *   NULL), so no inverse permute is needed.
  * labels_out: device int32[B*H]; stats_out: device float[B*H*3] (may be NULL
  * when modes_in is given).  ws must hold svg_workspace_bytes(geom, in,
  * modes_in ? 0 : n_rows, flags) bytes, 256-byte aligned.

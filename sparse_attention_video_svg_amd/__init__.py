@@ -396,15 +396,17 @@ def svg_sparse_attention(geom, q, k, v, o, modes, ranges, head_order, qp=None, k
         _check_shape(geom, t, name)
     if k.stride() != q.stride() or v.stride() != q.stride():
         raise ValueError("q, k and v must share strides")
-    if qp is not None and (kp.stride() != qp.stride() or vp.stride() != qp.stride()):
-        raise ValueError("qp, kp and vp must share strides")
+    if kp is not None and (vp is None or vp.stride() != kp.stride()):
+        raise ValueError("kp and vp must both be given and share strides")
+    if qp is not None and (kp is None or qp.stride() != kp.stride()):
+        raise ValueError("qp needs kp and vp with the same strides")
     din = _dtype_code(q)
     BM, BN = svg_tile_config(din, geom.d)
     _check_tile_args(geom, BM, BN, modes, ranges, head_order)
     g = geom.c()
     _check(_lib().svg_sparse_attention(
         ctypes.byref(g), din, _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _strides(q), _ptr(qp), _ptr(kp), _ptr(vp),
-        _strides(qp), _ptr(o), _strides(o), _ptr(op), _strides(op), _ptr(modes), _ptr(ranges), _ptr(head_order),
+        _strides(kp), _ptr(o), _strides(o), _ptr(op), _strides(op), _ptr(modes), _ptr(ranges), _ptr(head_order),
         BM, BN, flags, _stream(stream)))
 
 

@@ -192,9 +192,9 @@ WsLayout ws_layout(const KGeom& g, svg_dtype dtype, int32_t n_rows, int32_t flag
       off = align256(off + sizeof(float) * (size_t)BH);
     }
   } else if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
-    // token-major Q, K, V in the input dtype, then O sized for fp32 output
+    // token-major K and V in the input dtype
     w.perm_tensor_bytes = align256((size_t)BH * g.L * g.d * elt_bytes(dtype));
-    off += 3 * w.perm_tensor_bytes + align256((size_t)BH * g.L * g.d * 4);
+    off += 2 * w.perm_tensor_bytes;
   }
   w.total = off;
   return w;
@@ -240,12 +240,14 @@ svg_status validate_attention(const KGeom& g, svg_dtype in, svg_dtype out, const
   TRY(check_strides(s, g, ei, "q/k/v"));
   TRY(check_strides(so, g, eo, "o"));
   if (!(flags & SVG_FLAG_VIRTUAL_PERMUTE)) {
-    TRY(check_ptr(qp, "qp", 16));
+    // K and V copies are required; Q and O copies are optional (NULL: those
+    // rows go through the index map)
+    if (qp) TRY(check_ptr(qp, "qp", 16));
     TRY(check_ptr(kp, "kp", 16));
     TRY(check_ptr(vp, "vp", 16));
-    TRY(check_ptr(op, "op", 16));
+    if (op) TRY(check_ptr(op, "op", 16));
     TRY(check_strides(sp, g, ei, "qp/kp/vp"));
-    TRY(check_strides(sop, g, eo, "op"));
+    if (op) TRY(check_strides(sop, g, eo, "op"));
   }
   TRY(check_ptr(modes, "modes", 4));
   if (check_lists) {  // svg_layer_forward places them in its own workspace
@@ -454,8 +456,10 @@ svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out,
   const svg_strides sp{(int64_t)g.H * g.L * g.d, (int64_t)g.L * g.d, g.d};
   // workspace pointers (ws is the caller's, 256-byte aligned, or the fixed
   // scratch, whose address is only taken once every argument has passed)
+  // explicit layout: token-major copies of K and V only (Q is read and O
+  // written through the index map by the attention kernel)
   auto perm_at = [&](int t) -> void* { return virt ? nullptr : ws_at<char>(ws, w.perm) + t * w.perm_tensor_bytes; };
-  TRY(validate_attention(g, in, out, q, k, v, s, perm_at(0), perm_at(1), perm_at(2), sp, o, so, perm_at(3), sp,
+  TRY(validate_attention(g, in, out, q, k, v, s, nullptr, perm_at(0), perm_at(1), sp, o, so, nullptr, sp,
                          profile ? labels_out : modes_in, nullptr, nullptr, BM, BN, flags & SVG_FLAG_VIRTUAL_PERMUTE,
                          false));
   hipError_t e = apply_topology(&g);
@@ -464,7 +468,7 @@ svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out,
     e = static_scratch(&ws);
     if (e != hipSuccess) return hip_fail(e, "svg_layer_forward_noalloc (scratch address)");
   }
-  void *qp = perm_at(0), *kp = perm_at(1), *vp = perm_at(2), *op = perm_at(3);
+  void *kp = perm_at(0), *vp = perm_at(1);
   int32_t* ranges = ws_at<int32_t>(ws, w.ranges);
   int32_t* order = ws_at<int32_t>(ws, w.order);
   hipStream_t st = (hipStream_t)stream;
@@ -498,20 +502,16 @@ svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out,
     return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_layer_forward (fp8 attention)");
   }
   if (!virt) {
-    const void* src[3] = {q, k, v};
-    void* dst[3] = {qp, kp, vp};
-    for (int t = 0; t < 3; ++t) {
+    const void* src[2] = {k, v};
+    void* dst[2] = {kp, vp};
+    for (int t = 0; t < 2; ++t) {
       e = launch_permute(g, ei, src[t], s, dst[t], sp, modes, 0, st);
       if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (permute)");
     }
   }
-  AttnPtrs a{q, k, v, qp, kp, vp, o, op, s, sp, so, sp, modes, ranges, order, flags};
+  AttnPtrs a{q, k, v, nullptr, kp, vp, o, nullptr, s, sp, so, sp, modes, ranges, order, flags};
   e = run_attention(g, in, out, a, st);
   if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (attention)");
-  if (!virt) {
-    e = launch_permute(g, eo, op, sp, o, so, modes, 1, st);
-    if (e != hipSuccess) return hip_fail(e, "svg_layer_forward (inverse permute)");
-  }
   return SVG_OK;
 }
 

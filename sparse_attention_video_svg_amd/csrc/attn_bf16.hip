@@ -44,17 +44,23 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   constexpr int BMW = 32 * WAVES;
   const int hh = lane >> 5;
   const int b = bh / g.H, h = bh % g.H;
-  const bool use_p = mode == SVG_TEMPORAL && !VIRT;
-  const svg_strides sin = use_p ? a.sp : a.s;
-  const svg_strides sout = use_p ? a.sop : a.so;
-  const int64_t ibase = (int64_t)b * sin.b + (int64_t)h * sin.h;
+  // temporal heads: K, V from their token-major copies (VIRT: through the
+  // index map); Q and O from / to their copies when the caller gave them,
+  // else through the index map (rows are then read and written once each)
+  const bool temporal = mode == SVG_TEMPORAL;
+  const bool use_p = temporal && !VIRT;
+  const bool q_p = use_p && a.qp != nullptr, o_p = use_p && a.op != nullptr;
+  const svg_strides skv = use_p ? a.sp : a.s, sq = q_p ? a.sp : a.s, sout = o_p ? a.sop : a.so;
+  const int64_t ibase = (int64_t)b * skv.b + (int64_t)h * skv.h;
   const int64_t obase = (int64_t)b * sout.b + (int64_t)h * sout.h;
-  const __bf16* Q = static_cast<const __bf16*>(use_p ? a.qp : a.q) + ibase;
+  const __bf16* Q = static_cast<const __bf16*>(q_p ? a.qp : a.q) + (int64_t)b * sq.b + (int64_t)h * sq.h;
   const __bf16* K = static_cast<const __bf16*>(use_p ? a.kp : a.k) + ibase;
   const __bf16* V = static_cast<const __bf16*>(use_p ? a.vp : a.v) + ibase;
-  char* O = static_cast<char*>(use_p ? a.op : a.o);
+  char* O = static_cast<char*>(o_p ? a.op : a.o);
   constexpr int OE = OUT_BF16 ? 2 : 4;  // output element bytes
-  auto phys = [&g](int r) { return VIRT ? perm_inv_row(g, r) : r; };
+  const bool q_map = temporal && !q_p, o_map = temporal && !o_p;
+  auto qrow = [&g, q_map](int r) { return q_map ? perm_inv_row(g, r) : r; };
+  auto orow_of = [&g, o_map](int r) { return o_map ? perm_inv_row(g, r) : r; };
 
   const int4 rg = reinterpret_cast<const int4*>(a.ranges)[(int64_t)bh * nQT + qt];
 
@@ -63,12 +69,12 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   const bool valid = xq < g.L;
   const int xqc = valid ? xq : g.L - 1;
   bf16x8 qf[D / 16];
-  load_q<D>(qf, Q + (int64_t)phys(xqc) * sin.x, hh);
+  load_q<D>(qf, Q + (int64_t)qrow(xqc) * sq.x, hh);
   int lo, hi;
   row_interval(g, mode, xqc, lo, hi);
 
   Flash<D> st;
-  run_sweep<D, VIRT, WAVES, STAGES>(st, qf, K, V, sin.x, g, rg, lo, hi, valid, lds, wave, lane);
+  run_sweep<D, VIRT, WAVES, STAGES>(st, qf, K, V, skv.x, g, rg, lo, hi, valid, lds, wave, lane);
 
   // Epilogue: lane (query, h) holds dims 32*db + 8*(r/4) + 4*h + r%4.
   const float l_tot = half_sum(st.l_part);
@@ -80,7 +86,7 @@ __device__ __forceinline__ void attn_tile(const KGeom& g, const AttnPtrs& a, int
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
   const int xo = qt * BMW + wave * 32 + (lid & 31), ho = lid >> 5;
   if (xo < g.L) {
-    char* orow = O + (obase + (int64_t)phys(xo) * sout.x) * OE;
+    char* orow = O + (obase + (int64_t)orow_of(xo) * sout.x) * OE;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll

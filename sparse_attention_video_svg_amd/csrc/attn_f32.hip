@@ -36,20 +36,23 @@ __global__ __launch_bounds__(64) void k_attn_f32(KGeom g, AttnPtrs a, int32_t BM
   const int mode = a.modes[bh];
   const bool temporal = (mode == SVG_TEMPORAL);
   const bool virt = temporal && (a.flags & SVG_FLAG_VIRTUAL_PERMUTE);
+  // temporal heads: K, V from their token-major copies (or through the index
+  // map), Q and O from / to their copies when given, else through the map
   const bool use_p = temporal && !virt;
-  const svg_strides sin = use_p ? a.sp : a.s;
-  const svg_strides sout = use_p ? a.sop : a.so;
-  const float* Q = static_cast<const float*>(use_p ? a.qp : a.q) + (int64_t)b * sin.b + (int64_t)h * sin.h;
-  const float* K = static_cast<const float*>(use_p ? a.kp : a.k) + (int64_t)b * sin.b + (int64_t)h * sin.h;
-  const float* V = static_cast<const float*>(use_p ? a.vp : a.v) + (int64_t)b * sin.b + (int64_t)h * sin.h;
-  float* O = static_cast<float*>(use_p ? a.op : a.o) + (int64_t)b * sout.b + (int64_t)h * sout.h;
-  auto phys = [&](int r) { return virt ? perm_inv_row(g, r) : r; };
-  const int64_t orow = (int64_t)phys(x) * sout.x;
+  const bool q_p = use_p && a.qp != nullptr, o_p = use_p && a.op != nullptr;
+  const svg_strides skv = use_p ? a.sp : a.s, sq = q_p ? a.sp : a.s, sout = o_p ? a.sop : a.so;
+  const float* Q = static_cast<const float*>(q_p ? a.qp : a.q) + (int64_t)b * sq.b + (int64_t)h * sq.h;
+  const float* K = static_cast<const float*>(use_p ? a.kp : a.k) + (int64_t)b * skv.b + (int64_t)h * skv.h;
+  const float* V = static_cast<const float*>(use_p ? a.vp : a.v) + (int64_t)b * skv.b + (int64_t)h * skv.h;
+  float* O = static_cast<float*>(o_p ? a.op : a.o) + (int64_t)b * sout.b + (int64_t)h * sout.h;
+  auto phys = [&](int r) { return virt ? perm_inv_row(g, r) : r; };                      // K, V rows
+  auto qrow = [&](int r) { return temporal && !q_p ? perm_inv_row(g, r) : r; };
+  const int64_t orow = (int64_t)(temporal && !o_p ? perm_inv_row(g, x) : x) * sout.x;
   if (mode == SVG_SKIP) {
     for (int c = lane; c < D; c += 64) O[orow + c] = 0.f;
     return;
   }
-  for (int c = lane; c < D; c += 64) qs[c] = Q[(int64_t)phys(x) * sin.x + c];
+  for (int c = lane; c < D; c += 64) qs[c] = Q[(int64_t)qrow(x) * sq.x + c];
   __syncthreads();
   int lo, hi;
   row_interval(g, mode, x, lo, hi);
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(KGeom g, AttnPtrs a, int32_t BM
     const bool act = key_active(g, key, lo, hi);
     double s = -INFINITY;
     if (act) {
-      const float* kr = K + (int64_t)phys(key) * sin.x;
+      const float* kr = K + (int64_t)phys(key) * skv.x;
       double dot = 0.0;
       for (int c = 0; c < D; ++c) dot = fma((double)qs[c], (double)kr[c], dot);
       s = dot * (double)g.scale;
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(KGeom g, AttnPtrs a, int32_t BM
     for (int e = 0; e < 64; ++e) {
       const double pe = ps[e];
       if (pe != 0.0) {
-        const float* vr = V + (int64_t)phys(kb + e) * sin.x;
+        const float* vr = V + (int64_t)phys(kb + e) * skv.x;
         acc0 = fma(pe, (double)vr[lane], acc0);
         if (D == 128) acc1 = fma(pe, (double)vr[lane + 64], acc1);
       }

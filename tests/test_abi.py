@@ -83,7 +83,8 @@ def test_workspace_bytes_grows_with_rows_and_explicit_permutation():
     c = svg.svg_workspace_bytes(g, svg.BF16, 16, 0)
     assert 0 < a < b < c
     L = g.L
-    assert c - b >= 3 * g.H * L * g.d * 2 + g.H * L * g.d * 4
+    # the explicit layout holds token-major copies of K and V (bf16)
+    assert c - b >= 2 * g.H * L * g.d * 2
     with pytest.raises(svg.SvgError):
         svg.svg_workspace_bytes(g, svg.BF16, g.N * g.F + 1, 0)
     with pytest.raises(svg.SvgError):
@@ -107,12 +108,12 @@ BM_BF16, BN_BF16 = svg.svg_tile_config(svg.BF16, 128)
 
 
 def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, modes=A, ranges=A, order=A,
-                   BM=BM_BF16, BN=BN_BF16, flags=0, qp=A, sp=None):
+                   BM=BM_BF16, BN=BN_BF16, flags=0, qp=A, kp=A, sp=None):
     gc = g.c()
     s = s or strides()
     so = so or strides()
     sp = sp or strides()
-    return raw().svg_sparse_attention(ctypes.byref(gc), din, dout, q, A, A, s, qp, A, A, sp, o, so, A, sp, modes,
+    return raw().svg_sparse_attention(ctypes.byref(gc), din, dout, q, A, A, s, qp, kp, A, sp, o, so, A, sp, modes,
                                       ranges, order, BM, BN, flags, None)
 
 
@@ -120,7 +121,7 @@ def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, mo
     (dict(q=None), E_INVALID), (dict(q=A + 8), E_INVALID), (dict(o=None), E_INVALID),
     (dict(modes=None), E_INVALID), (dict(ranges=None), E_INVALID), (dict(order=None), E_INVALID),
     (dict(BM=64), E_UNSUPPORTED), (dict(BN=128), E_UNSUPPORTED), (dict(din=svg.F32, dout=svg.BF16), E_UNSUPPORTED),
-    (dict(din=5), E_INVALID), (dict(flags=4), E_INVALID), (dict(qp=None), E_INVALID),
+    (dict(din=5), E_INVALID), (dict(flags=4), E_INVALID), (dict(kp=None), E_INVALID), (dict(qp=A + 8), E_INVALID),
     (dict(s=svg._Strides(0, 0, 64)), E_INVALID), (dict(s=svg._Strides(0, 0, 132)), E_INVALID),
     (dict(so=svg._Strides(-8, 0, 128)), E_INVALID),
 ])

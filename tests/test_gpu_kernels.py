@@ -87,7 +87,10 @@ def test_build_blocks_bit_exact(N, F, T, a1, a2, W, St, BM, BN):
 
 
 def run_attention(g, q, k, v, modes_np, out_dtype, virtual):
-    """Tile lists + (explicit or virtual) layout transformation + attention."""
+    """Tile lists + layout transformation + attention.  virtual: True (index
+    map only), False (token-major copies of Q, K, V and O, O permuted back) or
+    "kv" (copies of K and V only, Q and O through the index map: the layer's
+    explicit path)."""
     din = svg.BF16 if q.dtype == torch.bfloat16 else svg.F32
     BM, BN = svg.svg_tile_config(din, g.d)
     BH = g.B * g.H
@@ -97,8 +100,13 @@ def run_attention(g, q, k, v, modes_np, out_dtype, virtual):
     order = torch.empty(BH, dtype=torch.int32, device="cuda")
     svg.svg_build_blocks(g, modes, BM, BN, ranges, order)
     o = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
-    if virtual:
+    if virtual is True:
         svg.svg_sparse_attention(g, q, k, v, o, modes, ranges, order, flags=svg.VIRTUAL_PERMUTE)
+    elif virtual == "kv":
+        kp, vp = (torch.empty_like(t) for t in (k, v))
+        for s_, d_ in ((k, kp), (v, vp)):
+            svg.svg_layout_permute(g, s_, d_, modes=modes)
+        svg.svg_sparse_attention(g, q, k, v, o, modes, ranges, order, kp=kp, vp=vp)
     else:
         qp, kp, vp = (torch.empty_like(t) for t in (q, k, v))
         for s_, d_ in ((q, qp), (k, kp), (v, vp)):
@@ -121,7 +129,7 @@ ATT_CASES = [
 
 
 @pytest.mark.parametrize("case", ATT_CASES)
-@pytest.mark.parametrize("virtual", [False, True])
+@pytest.mark.parametrize("virtual", [False, True, "kv"])
 def test_attention_all_modes(case, virtual):
     dt, N, F, T, d, a1, a2, W, St = case
     H = 6
@@ -149,8 +157,10 @@ def test_virtual_equals_explicit_and_deterministic():
     a = run_attention(g, q, k, v, MODES6, torch.bfloat16, False)
     b = run_attention(g, q, k, v, MODES6, torch.bfloat16, True)
     c = run_attention(g, q, k, v, MODES6, torch.bfloat16, True)
+    e = run_attention(g, q, k, v, MODES6, torch.bfloat16, "kv")
     assert np.array_equal(a, b)
     assert np.array_equal(b, c)
+    assert np.array_equal(a, e)
 
 
 @pytest.mark.parametrize("dt,N,F,T,d,a1,a2", [
@@ -192,7 +202,7 @@ LAYOUT_CASES = [
 
 
 @pytest.mark.parametrize("case", LAYOUT_CASES)
-@pytest.mark.parametrize("virtual", [False, True])
+@pytest.mark.parametrize("virtual", [False, True, "kv"])
 def test_attention_strided_batched_and_degenerate(case, virtual):
     """B = 2 with Q, K, V, O as [B, L, H, d] memory viewed as [B, H, L, d]
     (token-interleaved heads), and degenerate geometries: a single frame, one
@@ -217,8 +227,13 @@ def test_attention_strided_batched_and_degenerate(case, virtual):
     order = torch.empty(B * H, dtype=torch.int32, device="cuda")
     svg.svg_build_blocks(g, modes_t, BM, BN, ranges, order)
     o = interleaved(np.full((B * H, L, d), np.nan, dtype=np.float32), torch.bfloat16)
-    if virtual:
+    if virtual is True:
         svg.svg_sparse_attention(g, q, k, v, o, modes_t, ranges, order, flags=svg.VIRTUAL_PERMUTE)
+    elif virtual == "kv":
+        kp, vp = (torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+        for s_, d_ in ((k, kp), (v, vp)):
+            svg.svg_layout_permute(g, s_, d_, modes=modes_t)
+        svg.svg_sparse_attention(g, q, k, v, o, modes_t, ranges, order, kp=kp, vp=vp)
     else:
         qp, kp, vp = (torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
         for s_, d_ in ((q, qp), (k, kp), (v, vp)):
