@@ -126,11 +126,12 @@ __device__ __forceinline__ f32x16 score_block(const __bf16* lds_k, const bf16x8*
 // the K fragments read kAhead steps before their MFMAs, so LDS latency hides
 // behind matrix work instead of stalling every pair of MFMAs.
 // With ACC the products are added to s0, s1 instead of replacing them.
-template <int D, bool ACC = false>
+// AHEAD: K fragment steps read ahead (d 64 has four steps and a
+// 128-register budget: one).
+template <int D, bool ACC = false, int AHEAD = (D == 64 ? 1 : 3)>
 __device__ __forceinline__ void score_tile(const __bf16* lds_k, const bf16x8* qf, int lane, f32x16& s0, f32x16& s1) {
   using C = TileCfg<D>;
-  // (d 64 has four steps and a 128-register budget: one step ahead)
-  constexpr int KS = D / 16, kAhead = D == 64 ? 1 : 3;
+  constexpr int KS = D / 16, kAhead = AHEAD;
   const int hh = lane >> 5;
   const int m0 = lane & 31, m1 = 32 + (lane & 31);
   const int sw0 = C::swz_k(m0), sw1 = C::swz_k(m1);

@@ -109,8 +109,10 @@ __global__ __launch_bounds__(512, 4) void k_km_assign(KGeom g, const __bf16* __r
       ll.template load1<0>(g, (ct + 1) * kBN, lds[sg ^ 1][1], wave, lane);
     }
     f32x16 a0, a1;
-    score_tile<D>(lds[sg][0], qf, lane, a0, a1);
-    score_tile<D, true>(lds[sg][1], qf, lane, a0, a1);
+    // (one step ahead: the kernel is held to 128 registers for two
+    // workgroups per CU)
+    score_tile<D, false, 1>(lds[sg][0], qf, lane, a0, a1);
+    score_tile<D, true, 1>(lds[sg][1], qf, lane, a0, a1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
