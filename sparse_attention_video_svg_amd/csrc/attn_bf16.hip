@@ -381,24 +381,26 @@ static hipError_t launch_sweeps(const KGeom& g, const __bf16* q, const __bf16* k
                                 const int32_t* rows, int32_t n_rows, int32_t ksplit, const int32_t* ord_x,
                                 const int32_t* ord_r, const int32_t* modes, int32_t nstates, float* acc, float* ml,
                                 hipStream_t st) {
-  if constexpr (D == 64)
+  if constexpr (D == 64) {
     return launch_multi<D>(g, q, k, v, s, rows, ord_x, ord_r, n_rows, ksplit, modes, nstates, acc, ml, st);
-  for (int32_t i = 0; i < nstates; ++i) {
-    hipError_t e;
-    // masks with short runs per row take workgroups of kProfWavesBand waves (fewer rows, so the union of
-    // their runs stays close to each row's own); full attention the attention kernel's 8
-    if (modes[i] == SVG_TEMPORAL)
-      e = launch_prof<D, true, kProfWavesBand>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, SVG_TEMPORAL, i,
-                                               nstates, acc, ml, st);
-    else if (modes[i] == SVG_FULL)
-      e = launch_prof<D, false, kAttnWaves>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates, acc,
-                                            ml, st);
-    else
-      e = launch_prof<D, false, kProfWavesBand>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates,
-                                                acc, ml, st);
-    if (e != hipSuccess) return e;
+  } else {
+    for (int32_t i = 0; i < nstates; ++i) {
+      hipError_t e;
+      // masks with short runs per row take workgroups of kProfWavesBand waves (fewer rows, so the union of
+      // their runs stays close to each row's own); full attention the attention kernel's 8
+      if (modes[i] == SVG_TEMPORAL)
+        e = launch_prof<D, true, kProfWavesBand>(g, q, k, v, s, ord_x, ord_r, n_rows, ksplit, SVG_TEMPORAL, i,
+                                                 nstates, acc, ml, st);
+      else if (modes[i] == SVG_FULL)
+        e = launch_prof<D, false, kAttnWaves>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i, nstates,
+                                              acc, ml, st);
+      else
+        e = launch_prof<D, false, kProfWavesBand>(g, q, k, v, s, rows, nullptr, n_rows, ksplit, modes[i], i,
+                                                  nstates, acc, ml, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  return hipSuccess;
 }
 
 hipError_t launch_sample_sweeps(const KGeom& g, const void* q, const void* k, const void* v, svg_strides s,
