@@ -473,7 +473,19 @@ def main():
     torch.cuda.synchronize()
     perm_all_ms = pa.elapsed_time(pb) / 5
     perm_all_gbs = 2.0 * q.numel() * q.element_size() / (perm_all_ms * 1e-3) / 1e9
-    del qa
+    # a6 on its own as well (the layer writes temporal heads' outputs in
+    # place through the index map instead): the inverse of the whole tensor
+    qb = torch.empty_like(q)
+    for _ in range(2):
+        svg.svg_layout_permute(geom, qa, qb, inverse=True)
+    pa.record(stream)
+    for _ in range(5):
+        svg.svg_layout_permute(geom, qa, qb, inverse=True)
+    pb.record(stream)
+    torch.cuda.synchronize()
+    inv_all_ms = pa.elapsed_time(pb) / 5
+    inv_all_gbs = 2.0 * q.numel() * q.element_size() / (inv_all_ms * 1e-3) / 1e9
+    del qa, qb
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -526,6 +538,8 @@ def main():
         "permute_all_heads_ms": round(perm_all_ms, 4),
         "permute_all_heads_gbs": round(perm_all_gbs, 1),
         "permute_all_heads_frac_of_hbm": round(perm_all_gbs / 8000.0, 4),
+        "permute_inverse_all_heads_ms": round(inv_all_ms, 4),
+        "permute_inverse_all_heads_gbs": round(inv_all_gbs, 1),
         "effective_flops_per_layer": flops,
         "other_layout": None if alt is None else {
             "layout": "virtual" if alt[0] else "explicit",
