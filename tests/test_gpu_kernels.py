@@ -191,6 +191,35 @@ def test_profile_labels_bit_exact(dt, N, F, T, d, a1, a2):
         np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
 
 
+@pytest.mark.parametrize("d,seed", [(64, 11), (128, 12)])
+def test_profile_on_library_sampled_rows(d, seed):
+    """Row sampling and profiling through the library: svg_sample_rows draws
+    1 % of the video rows (fresh rows for a new seed), svg_profile_heads
+    labels the heads on them, equal to the oracle's labels on the same rows."""
+    N, F, T, a1, a2 = 8, 400, 16, 2, 40
+    kinds = [S.SPATIAL, S.TEMPORAL, S.SPATIAL, S.TEMPORAL]
+    H = len(kinds)
+    g = svg.Geom(B=1, H=H, d=d, N=N, F=F, T=T, a1=a1, a2=a2)
+    inp = S.small_config(N, F, T, H, d, a1, a2, kinds, seed=seed)
+    q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
+    count = -(-N * F // 100)
+    rows_np = svg.svg_sample_rows(g, count, seed)
+    assert not np.array_equal(rows_np, svg.svg_sample_rows(g, count, seed + 1))
+    rows = torch.from_numpy(rows_np).cuda()
+    labels = torch.empty(H, dtype=torch.int32, device="cuda")
+    stats = torch.empty(H * 3, dtype=torch.float32, device="cuda")
+    ws = svg.alloc_workspace(g, svg.BF16, rows.numel(), svg.VIRTUAL_PERMUTE)
+    print(f"\n[profile on library rows d={d} rows={count}]", flush=True)
+    svg.svg_profile_heads(g, q, k, v, rows, labels, stats, ws)
+    torch.cuda.synchronize()
+    lab, st = labels.cpu().numpy(), stats.cpu().numpy().reshape(H, 3)
+    og = ogeom(g)
+    for h in range(H):
+        want, ref = oracle.profile_head(og, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows_np)
+        assert lab[h] == want, (h, lab[h], want, st[h], ref)
+        np.testing.assert_allclose(st[h], ref, rtol=2e-2, atol=1e-4)
+
+
 LAYOUT_CASES = [
     # B, H, N, F, T, d, a1, a2, window, stripe, modes (B*H of them)
     (2, 3, 4, 50, 5, 128, 1, 6, 40, 60, [svg.SPATIAL, svg.TEMPORAL, svg.FULL, svg.WINDOW, svg.STRIPE, svg.SKIP]),
