@@ -51,21 +51,42 @@ struct SplitMix64 {
 
 }  // namespace
 
-// count distinct integers of [0, n), ascending, into out.
+// count distinct integers of [0, n), ascending, into out.  Membership of
+// the drawn set is a hash set while the sample is sparse (count < n / 64),
+// else a bitmap of n bits, which also yields the rows in order: host memory
+// stays within about n bytes either way.
 void sample_sorted(int64_t n, int32_t count, uint64_t seed, int32_t* out) {
   SplitMix64 rng{seed};
-  std::unordered_set<int32_t> seen;
-  seen.reserve((size_t)count * 2);
-  std::vector<int32_t> pick;
-  pick.reserve(count);
-  for (int64_t j = n - count; j < n; ++j) {
-    const int32_t t = (int32_t)rng.below((uint64_t)j + 1);
-    const int32_t keep = seen.insert(t).second ? t : (int32_t)j;
-    if (keep != t) seen.insert(keep);
-    pick.push_back(keep);
+  if ((int64_t)count * 64 < n) {
+    std::unordered_set<int32_t> seen;
+    seen.reserve((size_t)count * 2);
+    std::vector<int32_t> pick;
+    pick.reserve(count);
+    for (int64_t j = n - count; j < n; ++j) {
+      const int32_t t = (int32_t)rng.below((uint64_t)j + 1);
+      const int32_t keep = seen.insert(t).second ? t : (int32_t)j;
+      if (keep != t) seen.insert(keep);
+      pick.push_back(keep);
+    }
+    std::sort(pick.begin(), pick.end());
+    std::copy(pick.begin(), pick.end(), out);
+    return;
   }
-  std::sort(pick.begin(), pick.end());
-  std::copy(pick.begin(), pick.end(), out);
+  std::vector<uint64_t> bits((size_t)((n + 63) / 64), 0);
+  auto test_set = [&](int64_t x) {  // sets bit x, returns whether it was clear
+    uint64_t& w = bits[(size_t)(x >> 6)];
+    const uint64_t m = 1ull << (x & 63);
+    const bool was_clear = !(w & m);
+    w |= m;
+    return was_clear;
+  };
+  for (int64_t j = n - count; j < n; ++j) {
+    const int64_t t = rng.below((uint64_t)j + 1);
+    if (!test_set(t)) test_set(j);
+  }
+  int32_t k = 0;
+  for (size_t wi = 0; wi < bits.size(); ++wi)
+    for (uint64_t w = bits[wi]; w; w &= w - 1) out[k++] = (int32_t)(wi * 64 + __builtin_ctzll(w));
 }
 
 }  // namespace svg

@@ -74,6 +74,19 @@ def test_inclusion_rate_uniform_over_rows():
     assert abs(rate[-1] - 0.05) < 6 * math.sqrt(0.05 * 0.95 / draws)
 
 
+def test_inclusion_rate_uniform_sparse_draws():
+    # 10 of 1000 rows: the library keeps the drawn set in a hash set for
+    # sparse draws (a bitmap otherwise); each row drawn with probability 1/100
+    g, count, draws = geom(4, 250), 10, 20000
+    hits = np.zeros(1000)
+    for seed in range(draws):
+        r = svg.svg_sample_rows(g, count, seed)
+        assert np.all(np.diff(r) > 0)
+        hits[r] += 1
+    assert hits.sum() == count * draws
+    assert stats.chisquare(hits).pvalue > 1e-6
+
+
 def test_large_video_small_sample():
     # O(count) work whatever N*F is: 2^29 video rows, 1000 drawn
     r = svg.svg_sample_rows(geom(1 << 14, 1 << 15), 1000, 5)
