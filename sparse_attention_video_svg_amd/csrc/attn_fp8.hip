@@ -461,10 +461,7 @@ struct Flash8 {
 
   // s0, s1: raw scores (masked entries -inf), sl2 > 0: their log2 multiplier.
   __device__ __forceinline__ i32x8 softmax(const f32x16& s0, const f32x16& s1, float sl2) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = half_max(mx) * sl2;
+    const float mx = tile_max(s0, s1, sl2);
     const bool need = mx > m_ref + 2.0f;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       const float alpha = !need ? 1.f : (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx));
