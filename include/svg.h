@@ -25,6 +25,9 @@
  *  - All pointers except `geom`, `BM`, `BN`, `bytes` are DEVICE pointers owned
  *    by the caller.  The library never allocates, frees or keeps a pointer;
  *    scratch memory is the caller's workspace, sized by svg_workspace_bytes.
+ *  - No output of a call may share memory with an input of that call (the
+ *    kernels read rows that other workgroups of the same launch write); an
+ *    output starting at an input's address is rejected with SVG_E_INVALID.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work on it and returns; nothing synchronises.
  *  - Return value: SVG_OK, or an error status.  On any error nothing has been

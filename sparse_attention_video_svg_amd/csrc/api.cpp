@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "svg_internal.h"
 
 using namespace svg;
@@ -75,6 +77,16 @@ svg_status check_geom(const svg_geom* geom, KGeom* out) {
 svg_status check_ptr(const void* p, const char* name, size_t align) {
   if (!p) return fail(SVG_E_INVALID, "%s is NULL", name);
   if (((uintptr_t)p) % align) return fail(SVG_E_INVALID, "%s is not %zu-byte aligned", name, align);
+  return SVG_OK;
+}
+
+// An output starting where an input of the same call starts: the kernels
+// read rows that other workgroups of the same launch overwrite.  (Any overlap
+// is outside the contract; this catches the in-place call.)
+svg_status check_distinct(const void* out, const char* name, std::initializer_list<const void*> ins) {
+  if (!out) return SVG_OK;
+  for (const void* p : ins)
+    if (p == out) return fail(SVG_E_INVALID, "%s must not overlap an input of the call", name);
   return SVG_OK;
 }
 
@@ -249,6 +261,8 @@ svg_status validate_attention(const KGeom& g, svg_dtype in, svg_dtype out, const
     TRY(check_strides(sp, g, ei, "qp/kp/vp"));
     if (op) TRY(check_strides(sop, g, eo, "op"));
   }
+  TRY(check_distinct(o, "o", {q, k, v, qp, kp, vp}));
+  TRY(check_distinct(op, "op", {q, k, v, qp, kp, vp, o}));
   TRY(check_ptr(modes, "modes", 4));
   if (check_lists) {  // svg_layer_forward places them in its own workspace
     TRY(check_ptr(ranges, "ranges", 16));
@@ -431,6 +445,7 @@ svg_status layer_forward_impl(const svg_geom* geom, svg_dtype in, svg_dtype out,
   const bool fp8pv = flags & SVG_FLAG_FP8_PV;
   if (fp8 && in != SVG_BF16) return fail(SVG_E_UNSUPPORTED, "fp8 scores take bf16 inputs");
   if (fp8) flags |= SVG_FLAG_VIRTUAL_PERMUTE;  // the fp8 path reads temporal heads through the index map
+  TRY(check_distinct(o, "o", {q, k, v}));
   const bool profile = modes_in == nullptr;
   if (profile) {
     TRY(validate_profile(g, in, q, k, v, s, rows, n_rows, fallback_rel_mse, labels_out, stats_out));
@@ -668,6 +683,8 @@ svg_status svg_quantize_qk(const svg_geom* geom, svg_dtype dtype, const void* q,
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(q8, "q8", 16));
   TRY(check_ptr(k8, "k8", 16));
+  TRY(check_distinct(q8, "q8", {q, k}));
+  TRY(check_distinct(k8, "k8", {q, k, q8}));
   TRY(check_ptr(sq, "sq", 4));
   TRY(check_ptr(sk, "sk", 4));
   hipError_t e = launch_quant_qk(g, q, k, s, modes, q8, sq, k8, sk, (hipStream_t)stream);
@@ -692,6 +709,7 @@ svg_status svg_sparse_attention_fp8(const svg_geom* geom, svg_dtype out, const u
   TRY(check_ptr(o, "o", 16));
   TRY(check_strides(sv, g, 2, "v"));
   TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_distinct(o, "o", {q8, k8, v}));
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(ranges, "ranges", 16));
   TRY(check_ptr(head_order, "head_order", 4));
@@ -711,6 +729,7 @@ svg_status svg_quantize_v(const svg_geom* geom, svg_dtype dtype, const void* v, 
   TRY(check_strides(s, g, 2, "v"));
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(v8, "v8", 16));
+  TRY(check_distinct(v8, "v8", {v}));
   TRY(check_ptr(sv, "sv", 4));
   hipError_t e = launch_quant_v(g, v, s, modes, v8, sv, (hipStream_t)stream);
   return e == hipSuccess ? SVG_OK : hip_fail(e, "svg_quantize_v");
@@ -734,6 +753,7 @@ svg_status svg_sparse_attention_fp8_pv(const svg_geom* geom, svg_dtype out, cons
   TRY(check_ptr(sv, "sv", 4));
   TRY(check_ptr(o, "o", 16));
   TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_distinct(o, "o", {q8, k8, v8}));
   TRY(check_ptr(modes, "modes", 4));
   TRY(check_ptr(ranges, "ranges", 16));
   TRY(check_ptr(head_order, "head_order", 4));
@@ -793,6 +813,7 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* prm, svg_dtype 
   TRY(check_ptr(o, "o", 16));
   TRY(check_strides(s, g, 2, "q/k/v"));
   TRY(check_strides(so, g, elt_bytes(out), "o"));
+  TRY(check_distinct(o, "o", {q, k, v}));
   TRY(check_ptr(mu_q, "mu_q", 4));
   TRY(check_ptr(mu_k, "mu_k", 4));
   const Svg2Ws w = svg2_ws_layout(g, prm->C_q, prm->C_k);
@@ -808,7 +829,7 @@ svg_status svg2_forward(const svg_geom* geom, const svg2_params* prm, svg_dtype 
   int32_t* start_k = ws_at<int32_t>(ws, w.start_k);
   uint8_t* sel_w = sel ? sel : ws_at<uint8_t>(ws, w.sel);
   hipError_t e = apply_topology(&g);
-  if (!(flags & SVG2_FLAG_INIT_GIVEN)) {
+  if (e == hipSuccess && !(flags & SVG2_FLAG_INIT_GIVEN)) {
     e = launch_km_init(g, q, s, prm->C_q, mu_q, st);
     if (e == hipSuccess) e = launch_km_init(g, k, s, prm->C_k, mu_k, st);
   }

@@ -107,13 +107,17 @@ def strides(b=4 * 64 * 128, h=64 * 128 * 0 + 256 * 128, x=128):
 BM_BF16, BN_BF16 = svg.svg_tile_config(svg.BF16, 128)
 
 
-def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, modes=A, ranges=A, order=A,
-                   BM=BM_BF16, BN=BN_BF16, flags=0, qp=A, kp=A, sp=None):
+# distinct fake addresses of the tensors of one call
+Q, K, V, O, QP, KP, VP, OP = (A + i * 0x1000000 for i in range(8))
+
+
+def call_attention(g, din=svg.BF16, dout=svg.BF16, q=Q, s=None, o=O, so=None, modes=A, ranges=A, order=A,
+                   BM=BM_BF16, BN=BN_BF16, flags=0, qp=QP, kp=KP, sp=None, op=OP):
     gc = g.c()
     s = s or strides()
     so = so or strides()
     sp = sp or strides()
-    return raw().svg_sparse_attention(ctypes.byref(gc), din, dout, q, A, A, s, qp, kp, A, sp, o, so, A, sp, modes,
+    return raw().svg_sparse_attention(ctypes.byref(gc), din, dout, q, K, V, s, qp, kp, VP, sp, o, so, op, sp, modes,
                                       ranges, order, BM, BN, flags, None)
 
 
@@ -128,6 +132,44 @@ def call_attention(g, din=svg.BF16, dout=svg.BF16, q=A, s=None, o=A, so=None, mo
 def test_attention_validation(kw, status):
     assert call_attention(geom(), **kw) == status
     assert svg.svg_last_error()
+
+
+def test_outputs_must_not_overlap_inputs():
+    """An output starting at an input's address is rejected before any HIP
+    call.  Each call also carries an argument error that validation reports
+    after the overlap check, so none of them could reach the device even if
+    the overlap went unnoticed."""
+    g = geom().c()
+    L = raw()
+    s = strides()
+
+    def rejected_for_overlap(status):
+        return status == E_INVALID and "overlap" in svg.svg_last_error()
+
+    # attention (modes NULL: checked after the overlap)
+    for kw in (dict(o=Q), dict(o=KP), dict(op=V), dict(op=O)):
+        assert rejected_for_overlap(call_attention(geom(), modes=None, **kw)), kw
+    assert call_attention(geom(), modes=None) == E_INVALID and "modes" in svg.svg_last_error()
+    # the layer (rows NULL: checked after the overlap)
+    n_need = svg.svg_workspace_bytes(geom(), svg.BF16, 8, 0)
+    for o in (Q, K, V):
+        assert rejected_for_overlap(L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, o, s, None, 8,
+                                                        0.05, None, A, A, 0, A, n_need, None))
+        assert rejected_for_overlap(L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, o, s,
+                                                                None, 8, 0.05, None, A, A, 0, None))
+    # fp8 quantisation and attention, SVG2 forward
+    # (sk / sv NULL: checked after the overlap)
+    assert rejected_for_overlap(L.svg_quantize_qk(ctypes.byref(g), svg.BF16, Q, K, s, A, Q, A, KP, None, None))
+    assert rejected_for_overlap(L.svg_quantize_qk(ctypes.byref(g), svg.BF16, Q, K, s, A, QP, A, QP, None, None))
+    assert rejected_for_overlap(L.svg_quantize_v(ctypes.byref(g), svg.BF16, V, s, A, V, None, None))
+    # (modes / mu_q NULL: checked after the overlap)
+    assert rejected_for_overlap(L.svg_sparse_attention_fp8(ctypes.byref(g), svg.BF16, QP, A, KP, A, V, s, V, s, None,
+                                                           A, A, BM_BF16, BN_BF16, None))
+    assert rejected_for_overlap(L.svg_sparse_attention_fp8_pv(ctypes.byref(g), svg.BF16, QP, A, KP, A, VP, A, KP, s,
+                                                              None, A, A, BM_BF16, BN_BF16, None))
+    prm = svg._Svg2Params(32, 32, 2, 0.9)
+    assert rejected_for_overlap(L.svg2_forward(ctypes.byref(g), ctypes.byref(prm), svg.BF16, svg.BF16, Q, K, V, s, K,
+                                               s, 0, None, A, None, A, 1 << 40, None))
 
 
 def test_profile_validation():
@@ -164,11 +206,11 @@ def test_blocks_permute_layer_validation():
     assert L.svg_layout_permute(ctypes.byref(g), svg.BF16, None, s, A, s, None, 0, None) == E_INVALID
     assert L.svg_layout_permute(ctypes.byref(g), 3, A, s, A + 4096, s, None, 0, None) == E_INVALID
     # layer: too small a workspace, bad flags, missing labels when profiling
-    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A, 0, A,
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, O, s, A, 8, 0.05, None, A, A, 0, A,
                                1024, None) == E_WORKSPACE
-    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A, 2, A,
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, O, s, A, 8, 0.05, None, A, A, 2, A,
                                1 << 40, None) == E_INVALID
-    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, None, A, 0,
+    assert L.svg_layer_forward(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, O, s, A, 8, 0.05, None, None, A, 0,
                                A, 1 << 40, None) == E_INVALID
 
 
@@ -217,7 +259,7 @@ def test_svg2_validation():
         a = dict(base)
         a.update(kw)
         prm = svg._Svg2Params(a["Cq"], a["Ck"], a["it"], a["p"])
-        return L.svg2_forward(ctypes.byref(g), ctypes.byref(prm), a["din"], a["dout"], A, A, A, s, A, s, a["flags"],
+        return L.svg2_forward(ctypes.byref(g), ctypes.byref(prm), a["din"], a["dout"], Q, K, V, s, O, s, a["flags"],
                               a["mq"], a["mk"], None, a["ws"], a["wsb"], None)
 
     assert fwd(Cq=0) == E_INVALID
@@ -250,13 +292,13 @@ def test_fp8_pv_validation():
     g = geom().c()
     L = raw()
     s = strides()
-    assert L.svg_quantize_v(ctypes.byref(g), svg.F32, A, s, A, A, A, None) == E_UNSUPPORTED
-    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, A, None, A, None) == E_INVALID
-    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, A, A, None, None) == E_INVALID
-    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, A, s, None, A, A, None) == E_INVALID
+    assert L.svg_quantize_v(ctypes.byref(g), svg.F32, V, s, A, VP, A, None) == E_UNSUPPORTED
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, V, s, A, None, A, None) == E_INVALID
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, V, s, A, VP, None, None) == E_INVALID
+    assert L.svg_quantize_v(ctypes.byref(g), svg.BF16, V, s, None, VP, A, None) == E_INVALID
 
-    def att(BM=BM_BF16, BN=BN_BF16, v8=A, sv=A, out=svg.BF16):
-        return L.svg_sparse_attention_fp8_pv(ctypes.byref(g), out, A, A, A, A, v8, sv, A, s, A, A, A, BM, BN, None)
+    def att(BM=BM_BF16, BN=BN_BF16, v8=VP, sv=A, out=svg.BF16):
+        return L.svg_sparse_attention_fp8_pv(ctypes.byref(g), out, QP, A, KP, A, v8, sv, O, s, A, A, A, BM, BN, None)
 
     assert att(BM=BM_BF16 // 2) == E_UNSUPPORTED
     assert att(v8=None) == E_INVALID
@@ -280,15 +322,15 @@ def test_noalloc_layer_validation():
     s = strides()
     g = geom().c()
     assert svg.svg_noalloc_scratch_bytes() == 64 << 20
-    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, A, A,
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, O, s, A, 8, 0.05, None, A, A,
                                        svg.FP8_SCORES, None) == E_UNSUPPORTED
-    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, A, A, A, s, A, s, A, 8, 0.05, None, None,
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, Q, K, V, s, O, s, A, 8, 0.05, None, None,
                                        A, 0, None) == E_INVALID
-    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, None, A, A, s, A, s, A, 8, 0.05, None, A,
+    assert L.svg_layer_forward_noalloc(ctypes.byref(g), svg.BF16, svg.BF16, None, K, V, s, O, s, A, 8, 0.05, None, A,
                                        A, 0, None) == E_INVALID
     # 64 heads x 2048 tokens, all rows profiled: partials 64*2048*3*66*4 bytes > 64 MiB at one slice
     big = svg.Geom(B=1, H=64, d=64, N=2, F=1024, T=0, a1=1, a2=4, window=64, stripe=64).c()
     sb = svg._Strides(64 * 2048 * 64, 2048 * 64, 64)
-    assert L.svg_layer_forward_noalloc(ctypes.byref(big), svg.BF16, svg.BF16, A, A, A, sb, A, sb, A, 2048, 0.05, None,
+    assert L.svg_layer_forward_noalloc(ctypes.byref(big), svg.BF16, svg.BF16, Q, K, V, sb, O, sb, A, 2048, 0.05, None,
                                        A, A, 0, None) == E_WORKSPACE
     assert "scratch" in svg.svg_last_error()
