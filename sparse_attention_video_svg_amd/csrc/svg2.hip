@@ -484,14 +484,17 @@ struct Svg2Ptrs {
 // keys (segments of the cluster-ordered K and V), so only the last tile is
 // ragged (its rows clamp to the last key).  The LDS chunk layout and
 // swizzles are those of the contiguous loader; each lane's row comes from
-// the segment table through a cursor that only moves forward.
+// the segment table through a cursor that only moves forward.  The cursor's
+// segment (row = base + position) and the position where the next segment
+// starts stay in registers, so a tile that crosses no segment boundary
+// reads nothing from the table.
 template <int D>
 struct SegLoader {
   using C = TileCfg<D, 8>;
   const char* kb;
   const char* vb;
   uint32_t colk[C::LOADS], colv[C::LOADS];
-  int rr[C::LOADS], cur[C::LOADS];
+  int rr[C::LOADS], cur[C::LOADS], base[C::LOADS], next_y[C::LOADS];
 
   __device__ __forceinline__ void init(const __bf16* K, const __bf16* V, int wave, int lane) {
     kb = reinterpret_cast<const char*>(K);
@@ -501,28 +504,41 @@ struct SegLoader {
       const int p = min(i * 8 + wave, C::SEGS - 1) * 64 + lane;
       const int r = p / C::CR, pos = p % C::CR;
       rr[i] = r;
-      cur[i] = 0;
+      cur[i] = -1;  // the first load reads the table
+      base[i] = 0;
+      next_y[i] = INT_MIN;
       colk[i] = (uint32_t)((pos ^ C::swz_k(r)) * 16);
       colv[i] = (uint32_t)((pos ^ C::swz_v(r)) * 16);
     }
   }
 
+  // Every lookup in the LDS segment table comes before the first load is
+  // issued: an LDS read behind a direct-to-LDS load in flight would wait for
+  // that load to land (the compiler cannot tell the two apart).
   __device__ __forceinline__ void load(int t, const int2* sg, int ns, int nk, __bf16* lds_k, __bf16* lds_v,
                                        int wave) {
+    int64_t row[C::LOADS];
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int vpos = min(t * kBN + rr[i], nk - 1);
+      if (vpos >= next_y[i]) {  // into a later segment (or the first load)
+        int c = max(cur[i], 0);
+        while (c + 1 < ns && sg[c + 1].y <= vpos) ++c;
+        cur[i] = c;
+        const int2 e = sg[c];
+        base[i] = e.x - e.y;
+        next_y[i] = c + 1 < ns ? sg[c + 1].y : INT_MAX;
+      }
+      row[i] = (int64_t)(base[i] + vpos) * (D * 2);
+    }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int seg = i * 8 + wave;
       if (C::SEGS % 8 != 0 && seg >= C::SEGS) break;  // wave-uniform
-      const int vpos = min(t * kBN + rr[i], nk - 1);
-      int c = cur[i];
-      while (c + 1 < ns && sg[c + 1].y <= vpos) ++c;
-      cur[i] = c;
-      const int2 e = sg[c];
-      const int64_t row = (int64_t)(e.x + (vpos - e.y)) * (D * 2);
-      __builtin_amdgcn_global_load_lds((const void*)(kb + row + colk[i]), (SVG_LDS void*)(lds_k + seg * 512), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + row + colv[i]), (SVG_LDS void*)(lds_v + seg * 512), 16, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + row[i] + colk[i]), (SVG_LDS void*)(lds_k + seg * 512), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + row[i] + colv[i]), (SVG_LDS void*)(lds_v + seg * 512), 16,
+                                       0, 0);
     }
   }
 };
