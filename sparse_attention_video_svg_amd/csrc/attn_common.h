@@ -46,14 +46,31 @@ __device__ __forceinline__ void wait_vm() {
 // the lane's 32-bit offset (the saddr form of the load).  The last, ragged
 // tile clamps rows to L - 1; with VIRT the rows are gathered through the
 // token-major index map.
+//
+// With VIRT, token-major position x' = T + j*N + i (frame i, position j)
+// reads natural row T + i*F + j.  Moving 64 keys on moves i by 64 mod N and
+// j by 64 / N (one more when i wraps past N), so the natural row moves by a
+// fixed step, plus a fixed correction on a wrap: a tile that directly
+// follows the previous one (both all video rows, the new one not ragged)
+// takes each lane's row offset and i from the previous tile with adds; other
+// tiles (the first of a range, text rows, the ragged end) divide.  At d 64
+// the three registers per load do not fit the 128-register kernels, which
+// map every row.
 template <int D, bool VIRT, int WAVES = 4>
 struct KVLoader {
   using C = TileCfg<D, WAVES>;
+  static constexpr bool INC = VIRT && D == 128;  // incremental index map
+  static constexpr int NM = INC ? C::LOADS : 1;
   const char* kb;
   const char* vb;
   int64_t sxb;  // token stride in bytes
-  uint32_t offk[C::LOADS], offv[C::LOADS];
+  uint32_t offk[C::LOADS], offv[C::LOADS];  // VIRT: column bytes only
   int L;
+  int64_t vrow[NM];        // INC: byte offset of the lane's row of load i, last tile
+  int vfr[NM];             // INC: that row's frame i (meaningful for video rows)
+  int vlast;               // INC: first key of the last tile read
+  int64_t vstep, vwrap;    // INC: row-offset step per 64 keys, extra on a wrap
+  int vm64;                // INC: 64 mod N
 
   __device__ __forceinline__ void init(const __bf16* K, const __bf16* V, int64_t sx, int L_, int wave, int lane) {
     kb = reinterpret_cast<const char*>(K);
@@ -64,9 +81,49 @@ struct KVLoader {
     for (int i = 0; i < C::LOADS; ++i) {
       const int p = min(i * WAVES + wave, C::SEGS - 1) * 64 + lane;
       const int r = p / C::CR, pos = p % C::CR;
-      offk[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_k(r)) * 16);
-      offv[i] = (uint32_t)(r * sxb) + (uint32_t)((pos ^ C::swz_v(r)) * 16);
+      const uint32_t rb = INC ? 0u : (uint32_t)(r * sxb);
+      offk[i] = rb + (uint32_t)((pos ^ C::swz_k(r)) * 16);
+      offv[i] = rb + (uint32_t)((pos ^ C::swz_v(r)) * 16);
     }
+  }
+
+  // INC: the constants of the index map (after init).
+  __device__ __forceinline__ void init_map(const KGeom& g) {
+    const int q64 = (int)fastdiv(64, g.divN_mul, g.divN_shift);
+    vm64 = 64 - q64 * g.N;
+    vstep = ((int64_t)vm64 * g.F + q64) * sxb;
+    vwrap = ((int64_t)1 - (int64_t)g.N * g.F) * sxb;
+    vlast = INT_MIN / 2;
+  }
+
+  // INC: row offsets of every load of the tile at key kt0 into vrow.
+  __device__ __forceinline__ void map_rows(const KGeom& g, int kt0, int wave, int lane) {
+    if (kt0 == vlast + kBN && vlast >= g.T && kt0 + kBN <= L) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int fr = vfr[i] + vm64;
+        const bool wrap = fr >= g.N;
+        vfr[i] = wrap ? fr - g.N : fr;
+        vrow[i] += wrap ? vstep + vwrap : vstep;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int p = min(i * WAVES + wave, C::SEGS - 1) * 64 + lane;
+        int row = kt0 + p / C::CR;
+        row = row < L ? row : L - 1;
+        int nat = row, fr = 0;
+        if (row >= g.T) {
+          const int up = row - g.T;
+          const int j = (int)fastdiv(up, g.divN_mul, g.divN_shift);
+          fr = up - j * g.N;
+          nat = g.T + fr * g.F + j;
+        }
+        vfr[i] = fr;
+        vrow[i] = (int64_t)nat * sxb;
+      }
+    }
+    vlast = kt0;
   }
 
   // one tensor (K: which = 0, V: which = 1) of the tile at key kt0
@@ -81,6 +138,15 @@ struct KVLoader {
         if (C::SEGS % WAVES != 0 && seg >= C::SEGS) break;  // wave-uniform
         const uint32_t off = WHICH == 0 ? offk[i] : offv[i];
         __builtin_amdgcn_global_load_lds((const void*)(tb + off), (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
+      }
+    } else if (INC) {  // rows from map_rows
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int seg = i * WAVES + wave;
+        if (C::SEGS % WAVES != 0 && seg >= C::SEGS) break;  // wave-uniform
+        const uint32_t col = WHICH == 0 ? offk[i] : offv[i];
+        __builtin_amdgcn_global_load_lds((const void*)(base + vrow[INC ? i : 0] + col),
+                                         (SVG_LDS void*)(lds_t + seg * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
@@ -99,7 +165,8 @@ struct KVLoader {
     }
   }
 
-  __device__ __forceinline__ void load(const KGeom& g, int kt0, __bf16* lds_k, __bf16* lds_v, int wave, int lane) const {
+  __device__ __forceinline__ void load(const KGeom& g, int kt0, __bf16* lds_k, __bf16* lds_v, int wave, int lane) {
+    if constexpr (INC) map_rows(g, kt0, wave, lane);
     load1<0>(g, kt0, lds_k, wave, lane);
     load1<1>(g, kt0, lds_v, wave, lane);
   }
@@ -315,7 +382,7 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt0, int h
 // tiles go through a ring of STAGES LDS buffers: tile t + STAGES - 1 is in
 // flight while tile t is computed, with one barrier per tile.
 template <int D, bool VIRT, int WAVES, int STAGES>
-__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, const KVLoader<D, VIRT, WAVES>& ld,
+__device__ __forceinline__ void sweep(Flash<D>& st, const bf16x8* qf, KVLoader<D, VIRT, WAVES>& ld,
                                       const KGeom& g, int4 rg, int lo, int hi, bool valid,
                                       __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
   constexpr int PER_TILE = 2 * TileCfg<D, WAVES>::LOADS;  // load instructions per tile per wave
@@ -379,6 +446,7 @@ __device__ __forceinline__ void run_sweep(Flash<D>& st, const bf16x8* qf, const 
                                           __bf16 (*lds)[2][TileCfg<D>::TILE_ELEMS], int wave, int lane) {
   KVLoader<D, VIRT, WAVES> ld;
   ld.init(K, V, sx, g.L, wave, lane);
+  if constexpr (KVLoader<D, VIRT, WAVES>::INC) ld.init_map(g);
   if (rg.y > rg.x)
     ld.load(g, rg.x * kBN, lds[0][0], lds[0][1], wave, lane);
   else if (rg.w > rg.z)
