@@ -163,6 +163,27 @@ def test_virtual_equals_explicit_and_deterministic():
     assert np.array_equal(a, e)
 
 
+@pytest.mark.parametrize("N,F,T", [(64, 3, 0), (65, 2, 7), (100, 2, 5), (130, 1, 3), (7, 40, 70)])
+def test_index_map_frame_counts(N, F, T):
+    """Temporal heads through the index map (read incrementally from tile to
+    tile at d 128: a frame wrap on every tile, exactly one, or one every few
+    tiles, and ranges that start in the text prefix) give the same bits as
+    the token-major copies, and the oracle's outputs."""
+    d, a1, a2 = 128, 2, 3
+    g = svg.Geom(B=1, H=6, d=d, N=N, F=F, T=T, a1=a1, a2=a2, window=33, stripe=40)
+    kinds = [planted_kind(m) for m in MODES6]
+    inp = S.small_config(N, F, T, 6, d, a1, a2, kinds, seed=N * 7 + F + T, window=33, stripe=40)
+    q, k, v = (to_device(inp[n][None], torch.bfloat16) for n in "qkv")
+    a = run_attention(g, q, k, v, MODES6, torch.bfloat16, True)
+    b = run_attention(g, q, k, v, MODES6, torch.bfloat16, "kv")
+    assert np.array_equal(a, b)
+    og = ogeom(g)
+    rows = np.arange(g.L)
+    for h, mode in enumerate(MODES6):
+        ref = oracle.attention_rows(og, mode, inp["q"][h], inp["k"][h], inp["v"][h], scale_of(g), rows)
+        check_close(a[0, h], ref, "bf16", what=f"mode {mode} N {N}")
+
+
 @pytest.mark.parametrize("dt,N,F,T,d,a1,a2", [
     ("bf16", 6, 96, 0, 128, 2, 12), ("bf16", 5, 120, 20, 64, 1, 20), ("f32", 4, 64, 0, 64, 1, 8),
     ("bf16", 4, 50, 9, 128, 2, 7)])
