@@ -70,9 +70,11 @@ __global__ void k_km_split(int32_t C, int32_t D, const float* __restrict__ mu, _
 }
 
 // grid (ceil(L/256), BH), 8 waves x 32 tokens.  labels[bh*L + x].  The
-// scores x . hi and x . lo accumulate into one register pair; the half
-// squared norms sit in LDS; two workgroups share a CU, so one's loads
-// overlap the other's matrix work.
+// scores x . hi and x . lo accumulate into one register pair that starts at
+// -|mu|^2 / 2 of its centroids (the half squared norms sit in LDS, read four
+// at a time); each lane visits its centroids in increasing index order, so
+// a strict > keeps the lowest index among equal scores; two workgroups
+// share a CU, so one's loads overlap the other's matrix work.
 template <int D>
 __global__ __launch_bounds__(512, 4) void k_km_assign(KGeom g, const __bf16* __restrict__ x, svg_strides s,
                                                       int32_t C, const __bf16* __restrict__ hi,
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(512, 4) void k_km_assign(KGeom g, const __bf16* __r
                                                       int32_t* __restrict__ labels) {
   using TC = TileCfg<D, 8>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][TC::TILE_ELEMS];  // [stage][hi, lo]
-  __shared__ float hns[kSvg2MaxClusters];
+  __shared__ __attribute__((aligned(16))) float hns[kSvg2MaxClusters];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y;
@@ -109,21 +111,33 @@ __global__ __launch_bounds__(512, 4) void k_km_assign(KGeom g, const __bf16* __r
       ll.template load1<0>(g, (ct + 1) * kBN, lds[sg ^ 1][1], wave, lane);
     }
     f32x16 a0, a1;
+    // accumulator r of block kb2 holds centroid ct*64 + acc_key(kb2, r, hh):
+    // four consecutive centroids per group of four registers (entries past
+    // C are never selected)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 n0 = *reinterpret_cast<const f32x4*>(&hns[ct * kBN + 8 * g4 + 4 * hh]);
+      const f32x4 n1 = *reinterpret_cast<const f32x4*>(&hns[ct * kBN + 32 + 8 * g4 + 4 * hh]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0[4 * g4 + j] = -n0[j];
+        a1[4 * g4 + j] = -n1[j];
+      }
+    }
     // (one step ahead: the kernel is held to 128 registers for two
     // workgroups per CU)
-    score_tile<D, false, 1>(lds[sg][0], qf, lane, a0, a1);
+    score_tile<D, true, 1>(lds[sg][0], qf, lane, a0, a1);
     score_tile<D, true, 1>(lds[sg][1], qf, lane, a0, a1);
+    const bool full = (ct + 1) * kBN <= C;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int r = 0; r < 16; ++r) {
         const int c = ct * kBN + acc_key(kb2, r, hh);
-        if (c < C) {
-          const float v = (kb2 ? a1[r] : a0[r]) - hns[c];
-          if (v > best || (v == best && c < bidx)) {
-            best = v;
-            bidx = c;
-          }
+        const float v = kb2 ? a1[r] : a0[r];
+        if ((full || c < C) && v > best) {
+          best = v;
+          bidx = c;
         }
       }
     }
