@@ -1,5 +1,6 @@
-"""The layer captured in a HIP graph (torch.cuda.CUDAGraph) and replayed with
-new inputs and freshly sampled rows each time, with eager calls of the same
+"""The layer (bf16, the fixed-scratch entry point, FP8 scores, FP8 scores and
+P.V) captured in a HIP graph (torch.cuda.CUDAGraph) and replayed with new
+inputs and freshly sampled rows each time, with eager calls of the same
 layer between the replays: every replay's labels, statistics and outputs are
 bit-identical to the eager call on the same inputs (marked gpu).
 
@@ -38,23 +39,25 @@ def _host(outs):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("noalloc", [False, True])
-def test_layer_graph_replays_equal_eager(d, noalloc):
+@pytest.mark.parametrize("path", ["bf16", "noalloc", "fp8", "fp8pv"])
+def test_layer_graph_replays_equal_eager(d, path):
     g = svg.Geom(B=1, H=len(KINDS), d=d, N=6, F=400, T=16, a1=2, a2=40)
     count = 48
-    print(f"\n[graph capture: d {d}, noalloc {noalloc}]", flush=True)
+    noalloc = path == "noalloc"
+    flags = {"bf16": 0, "noalloc": 0, "fp8": svg.FP8_SCORES, "fp8pv": svg.FP8_SCORES | svg.FP8_PV}[path]
+    print(f"\n[graph capture: d {d}, {path}]", flush=True)
     q, k, v = _inputs(g, seed=100 + d)
     rows = torch.from_numpy(svg.svg_sample_rows(g, count, 1)).cuda()
     gout = _outputs(g)
-    ws_g = None if noalloc else svg.alloc_workspace(g, svg.BF16, count, 0)
-    ws_e = svg.alloc_workspace(g, svg.BF16, count, 0)
+    ws_g = None if noalloc else svg.alloc_workspace(g, svg.BF16, count, flags)
+    ws_e = svg.alloc_workspace(g, svg.BF16, count, flags)
 
     def layer(outs, ws):
         o, lab, st = outs
         if noalloc:
             svg.svg_layer_forward_noalloc(g, q, k, v, o, rows=rows, labels_out=lab, stats_out=st)
         else:
-            svg.svg_layer_forward(g, q, k, v, o, ws, rows=rows, labels_out=lab, stats_out=st)
+            svg.svg_layer_forward(g, q, k, v, o, ws, rows=rows, labels_out=lab, stats_out=st, flags=flags)
 
     # first call outside capture (reads the device topology, sets kernel
     # attributes), on a side stream as capture itself will run
