@@ -103,3 +103,58 @@ def test_layer_graph_replays_equal_eager(d, path):
         seen.add(got[0].tobytes()[:4096])
     # the replays saw the new inputs rather than repeating the captured ones
     assert len(seen) == 3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_svg2_graph_replays_equal_eager(d):
+    """svg2_forward (k-means of Q and K from the strided start, selection,
+    gathers, attention) captured and replayed on new inputs: outputs and
+    selections bit-identical to eager calls."""
+    g = svg.Geom(B=1, H=3, d=d, N=4, F=300, T=8)
+    C = 16
+    prm = svg.Svg2Params(C, C, 2, 0.9)
+    print(f"\n[svg2 graph capture: d {d}]", flush=True)
+
+    def inputs(seed):
+        inp = S.svg2_inputs(g.N, g.F, g.T, g.H, d, C, seed=seed)
+        return [torch.from_numpy(inp[n][None]).cuda().to(torch.bfloat16) for n in "qkv"]
+
+    q, k, v = inputs(5 + d)
+    ws_g = torch.empty(svg.svg2_workspace_bytes(g, prm), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws_g)
+
+    def bufs():
+        return (torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda"),
+                torch.empty(g.H * C * d, dtype=torch.float32, device="cuda"),
+                torch.empty(g.H * C * d, dtype=torch.float32, device="cuda"),
+                torch.zeros(g.H * C * C, dtype=torch.uint8, device="cuda"))
+
+    gb = bufs()
+
+    def fwd(b, ws):
+        o, mq, mk, sel = b
+        svg.svg2_forward(g, prm, q, k, v, o, mq, mk, ws, sel=sel)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd(gb, ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd(gb, ws_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        nq, nk, nv = inputs(50 + 10 * rep + d)
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_sel = gb[0].view(torch.int16).cpu().numpy(), gb[3].cpu().numpy()
+        eb = bufs()
+        fwd(eb, ws_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(got_sel, eb[3].cpu().numpy()), f"replay {rep}: selections differ"
+        assert np.array_equal(got_o, eb[0].view(torch.int16).cpu().numpy()), f"replay {rep}: outputs differ"
