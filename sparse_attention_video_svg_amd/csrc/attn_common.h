@@ -64,7 +64,7 @@ struct KVLoader {
   const char* kb;
   const char* vb;
   int64_t sxb;  // token stride in bytes
-  uint32_t offk[C::LOADS], offv[C::LOADS];  // VIRT: column bytes only
+  uint32_t offk[C::LOADS], offv[C::LOADS];  // row + column bytes in the tile (INC: column bytes only)
   int L;
   int64_t vrow[NM];        // INC: byte offset of the lane's row of load i, last tile
   int vfr[NM];             // INC: that row's frame i (meaningful for video rows)

@@ -24,7 +24,8 @@ namespace svg {
 // is the number of rows with a smaller key (keys are distinct).  Rows are
 // clamped into [T, L) as read, and ranks stay in [0, n_rows) whatever the
 // list holds, so a list that breaks the contract is never a memory error.
-// k_prof_rank_lds: all keys staged in LDS, each thread counts over them.
+// k_prof_rank_lds: all keys staged in LDS, four lanes per row each count
+// over a quarter of them.
 // k_prof_rank (more rows than fit): per frame, a binary search for the
 // rows at smaller positions, plus the row at the same position if its
 // frame comes earlier.
@@ -56,19 +57,25 @@ __global__ __launch_bounds__(256) void k_prof_rank_lds(KGeom g, const int32_t* _
     keys[r] = key;
   }
   __syncthreads();
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n_rows) return;
-  const int own = keys[r];
+  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
+  const int r = gt >> 2, q = gt & 3;  // row, quarter of the keys
+  const bool ok = r < n_rows;
+  const int own = ok ? keys[r] : 0;
   int rank = 0;
   // equal keys (a repeated row) are ranked by their index, so the ranks are
   // a permutation of [0, n_rows) for any list
-  for (int o = 0; o < n4; o += 4) {
-    const int4 k4 = *reinterpret_cast<const int4*>(keys + o);
-    rank += (k4.x < own || (k4.x == own && o < r)) + (k4.y < own || (k4.y == own && o + 1 < r)) +
-            (k4.z < own || (k4.z == own && o + 2 < r)) + (k4.w < own || (k4.w == own && o + 3 < r));
+  if (ok)
+    for (int o = 4 * q; o < n4; o += 16) {
+      const int4 k4 = *reinterpret_cast<const int4*>(keys + o);
+      rank += (k4.x < own || (k4.x == own && o < r)) + (k4.y < own || (k4.y == own && o + 1 < r)) +
+              (k4.z < own || (k4.z == own && o + 2 < r)) + (k4.w < own || (k4.w == own && o + 3 < r));
+    }
+  rank += __shfl_xor(rank, 1);
+  rank += __shfl_xor(rank, 2);
+  if (ok && q == 0) {
+    ord_x[rank] = sampled_row(g, rows[r]);
+    ord_r[rank] = r;
   }
-  ord_x[rank] = sampled_row(g, rows[r]);
-  ord_r[rank] = r;
 }
 
 __global__ void k_prof_rank(KGeom g, const int32_t* __restrict__ rows, int32_t n_rows, int32_t* __restrict__ ord_x,
@@ -244,11 +251,12 @@ __global__ __launch_bounds__(256) void k_search_finalize(int32_t d, int32_t n_ro
 
 hipError_t launch_profile_rank(const KGeom& g, const int32_t* rows, int32_t n_rows, int32_t* ord_x, int32_t* ord_r,
                                hipStream_t st) {
-  const dim3 grid((unsigned)((n_rows + 255) / 256));
   if (n_rows <= kRankLdsRows)
-    hipLaunchKernelGGL(k_prof_rank_lds, grid, dim3(256), 0, st, g, rows, n_rows, ord_x, ord_r);
+    hipLaunchKernelGGL(k_prof_rank_lds, dim3((unsigned)((4 * n_rows + 255) / 256)), dim3(256), 0, st, g, rows, n_rows,
+                       ord_x, ord_r);
   else
-    hipLaunchKernelGGL(k_prof_rank, grid, dim3(256), 0, st, g, rows, n_rows, ord_x, ord_r);
+    hipLaunchKernelGGL(k_prof_rank, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, st, g, rows, n_rows, ord_x,
+                       ord_r);
   return hipGetLastError();
 }
 
